@@ -1,0 +1,144 @@
+"""Pins of the oracle's per-token NVFP4 quantizer Q and its weight variant.
+
+What fixes Q here, independently of the oracle's code:
+  * a hand-derived worked example (tests/golden/nvfp4_row_worked_example.txt);
+  * the lossless special case: inputs already on the NVFP4 grid (block amax
+    6*2^j, row amax 6*2^i, 448*2^(j-i) an exact E4M3 value) dequantize to
+    themselves exactly, which pins the direction and size of both scales;
+  * invariants: the block that holds the row maximum gets scale 448 (0x7E);
+    an all-zero row gives g = 1, scales 0 and codes +0;
+  * the per-element error bound of the two-level scheme, with dequantization
+    done by lookup tables in the test (tests/npref.py), not by the oracle.
+"""
+import os
+
+import numpy as np
+
+import oracle
+from nvfp4_token_quant_amd import synth
+from tests import npref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load_worked_example():
+    fields = {}
+    for line in open(os.path.join(GOLDEN, "nvfp4_row_worked_example.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, *vals = line.split()
+        fields[name] = vals
+    x = synth.bf16_bits(np.array([float(v) for v in fields["x"]], np.float32))[None, :]
+    codes = np.array([int(v, 16) for v in fields["codes"]], np.uint8)
+    scales = np.array([int(v, 16) for v in fields["scales"]], np.uint8)
+    return x, codes, scales, float(fields["g"][0])
+
+
+def test_worked_example():
+    x, codes, scales, g = _load_worked_example()
+    c, S, gg = oracle.quantize_rows(x)
+    np.testing.assert_array_equal(c[0], codes)
+    np.testing.assert_array_equal(S[0], scales)
+    assert gg[0] == np.float32(g)
+
+
+def _fp4_exact_rows(rng, rows, K):
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    x = np.zeros((rows, K), np.float64)
+    for r in range(rows):
+        i = int(rng.integers(-20, 20))
+        top = int(rng.integers(0, K // 16))             # block holding the row amax
+        for b in range(K // 16):
+            j = i if b == top else i - int(rng.integers(0, 15))  # j in [i-14, i]
+            blk = rng.choice(mags, 16) * rng.choice([-1.0, 1.0], 16)
+            blk[rng.integers(0, 16)] = 6.0 * rng.choice([-1.0, 1.0])  # block amax 6*2^j
+            x[r, 16 * b:16 * b + 16] = blk * 2.0 ** j
+    return x.astype(np.float32)
+
+
+def test_lossless_on_grid_inputs():
+    rng = np.random.default_rng(3)
+    x = _fp4_exact_rows(rng, 64, 256)
+    c, S, g = oracle.quantize_rows(x)
+    xh = npref.dequant(c, S, g)
+    np.testing.assert_array_equal(xh, x.astype(np.float64))
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    np.testing.assert_array_equal(g.astype(np.float64), 2688.0 / amax)
+
+
+def test_row_max_block_gets_448_and_zero_rows():
+    rng = np.random.default_rng(4)
+    x = rng.standard_t(3, size=(50, 512)).astype(np.float32)
+    x[7] = 0.0
+    c, S, g = oracle.quantize_rows(x)
+    for r in range(50):
+        if r == 7:
+            assert g[r] == 1.0 and not S[r].any() and not c[r].any()
+            continue
+        b = int(np.argmax(np.abs(x[r]))) // 16
+        assert S[r, b] == 0x7E
+
+
+def test_tiny_row_clamps_global_scale():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 3] = np.float32(1e-38)            # 2688 / 1e-38 overflows binary32
+    c, S, g = oracle.quantize_rows(x)
+    assert g[0] == np.finfo(np.float32).max
+
+
+def _bound_check(x, c, S, g):
+    """|x - x^| <= half a grid step of |x r_b| times d_b / g (+4 ulp slack)."""
+    xh = npref.dequant(c, S, g)
+    d = np.repeat(npref.e4m3_values(S), 16, axis=-1)
+    gg = g.astype(np.float64)[:, None]
+    v = np.abs(x.astype(np.float64)) * gg / np.where(d > 0, d, 1.0)
+    step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+    bound = np.where(v <= 6, 0.5 * step * d / gg, np.abs(x) - 6 * d / gg)
+    bound = np.where(d > 0, bound, np.abs(x))
+    err = np.abs(x.astype(np.float64) - xh)
+    slack = 4 * np.spacing(np.abs(x).astype(np.float32)).astype(np.float64) + 1e-300
+    assert np.all(err <= bound * (1 + 1e-6) + slack)
+    # beyond-6 elements only occur where the E4M3 rounding of the scale went down
+    over = (v > 6) & (d > 0)
+    assert np.all(v[over] <= 6.0 * (1 + 1 / 16) + 1e-6)
+
+
+def test_error_bound_student_t_rows():
+    rng = np.random.default_rng(5)
+    x = rng.standard_t(3, size=(200, 1024)).astype(np.float32)
+    x[::17] *= np.float32(1e3)
+    x[5, :] *= np.float32(1e-30)
+    xb = synth.bf16_to_f32(synth.bf16_bits(x))
+    c, S, g = oracle.quantize_rows(synth.bf16_bits(x))
+    _bound_check(xb, c, S, g)
+
+
+def test_nibble_order_low_is_even_element():
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0] = 6.0     # code 7 in the low nibble of byte 0
+    x[0, 1] = -1.0    # code 0xA in the high nibble of byte 0
+    x[0, 15] = 0.5    # code 1 in the high nibble of byte 7
+    c, S, g = oracle.quantize_rows(x)
+    assert c[0, 0] == 0xA7 and c[0, 7] == 0x10 and S[0, 0] == 0x7E and g[0] == 448.0
+
+
+def test_group_quantizer_uses_whole_tensor_amax():
+    rng = np.random.default_rng(6)
+    w = rng.normal(0, 0.02, size=(3, 64, 128)).astype(np.float32)
+    w[1, 5, 7] = 1.0
+    c, S, g = oracle.quantize_groups(w)
+    for e in range(3):
+        assert g[e] == np.float32(2688.0) / np.float32(np.abs(w[e]).max())
+        # rows quantized with the group's g match the per-row quantizer fed that g
+        c2, S2 = oracle.quantize_rows_given_g(w[e], np.full(64, g[e], np.float32))
+        np.testing.assert_array_equal(c[e], c2)
+        np.testing.assert_array_equal(S[e], S2)
+        _bound_check(w[e], c[e], S[e], np.full(64, g[e], np.float32))
+
+
+def test_oracle_dequantize_matches_lut():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((8, 64)).astype(np.float32)
+    c, S, g = oracle.quantize_rows(x)
+    np.testing.assert_array_equal(oracle.dequantize(c, S, g), npref.dequant(c, S, g))
