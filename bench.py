@@ -1,0 +1,236 @@
+"""Benchmark of the NVFP4 fused-MoE layer on one MI355X.
+
+One step = one forward of the whole layer (per-token quantize, router top-k,
+expandInputRows permutation, GEMM1 + SwiGLU, re-quantization + GEMM2,
+finalize) over one batch of seeded synthetic tokens already resident in HBM.
+Default workload: the decode-shaped layer (T=64, H=2048, E=128, top-8,
+I=768).  Prints one JSON line.
+
+Timing: `steps` forwards after `warmup` untimed ones, bracketed by
+synchronizations; wall time gives `value` (tokens/s).  Every timed forward
+also records HIP events around its four kernels on its own stream, which give
+each kernel's mean duration; the dominant kernel's algorithmic bytes (or
+FLOPs) over that duration is `roofline.achieved`.  Expert weights rotate over
+`--rotate` copies so consecutive steps do not find them in the 256 MB
+Infinity Cache.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layer", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--T", type=int, default=None, help="tokens (default: the layer's)")
+    ap.add_argument("--fast-finalize", action="store_true",
+                    help="atomic (non-deterministic) finalize instead of the slot-ordered one")
+    ap.add_argument("--rotate", type=int, default=2, help="copies of the expert weights")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Hip:
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        P = ctypes.c_void_p
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        self.h.hipEventSynchronize.argtypes = [P]
+        self.h.hipEventDestroy.argtypes = [P]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X; no collectives are built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from nvfp4_token_quant_amd import binding, synth
+    from nvfp4_token_quant_amd.workloads import gpu_weights, to_device_bf16
+
+    binding.lib()  # fails loudly if the HIP library is missing
+    L = synth.LAYERS[args.layer]
+    T = args.T or L.T
+    H, I, E, k = L.H, L.I, L.E, L.k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: layer {args.layer} ({L.name}) T={T} H={H} E={E} k={k} I={I}", file=sys.stderr, flush=True)
+
+    x_bits = synth.activations(args.layer, T)
+    logits_np = synth.router_logits(args.layer, T)
+    x = to_device_bf16(x_bits, dev)
+    logits = torch.from_numpy(logits_np).to(dev)
+    weights = [gpu_weights(args.layer, device=dev)]
+    for _ in range(args.rotate - 1):
+        w0 = weights[0]
+        weights.append(binding.NvFp4Weights(*(t.clone() for t in (
+            w0.w13_codes, w0.w13_scales, w0.w13_gscale, w0.w2_codes, w0.w2_scales, w0.w2_gscale))))
+    det = not args.fast_finalize
+    max_tokens = max(T, L.max_tokens)
+    layers = []
+    for w in weights:
+        ly = binding.MoeLayer(max_tokens, H, I, E, k, deterministic=det)
+        ly.bind(w)
+        layers.append(ly)
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+
+    # routing statistics for the algorithmic byte / FLOP counts, from the GPU's own counts
+    layers[0].forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    counts = layers[0].read_buffer("COUNTS", torch.int32, (E,)).cpu().numpy()
+    active = int((counts > 0).sum())
+    R = T * k
+    w13_bytes = 2 * I * H * 0.5625 + 4
+    w2_bytes = H * I * 0.5625 + 4
+    stage_bytes = {
+        "prologue": T * H * 2 + T * E * 4 + T * (H * 0.5625 + 4) + R * 8,
+        "gemm1": active * w13_bytes + R * (H * 0.5625 + 4),
+        "gemm2": active * w2_bytes,
+        "finalize": T * H * 2,
+    }
+    stage_flops = {"prologue": 0.0, "gemm1": 2.0 * R * 2 * I * H, "gemm2": 2.0 * R * H * I,
+                   "finalize": 2.0 * R * H}
+    layer_bytes = active * (w13_bytes + w2_bytes) + T * H * 2 + T * E * 4 + T * H * 2
+    layer_flops = 6.0 * R * I * H
+
+    hip = Hip()
+    stages = ["prologue", "gemm1", "gemm2", "finalize"]
+    for i in range(args.warmup):
+        layers[i % len(layers)].forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
+    lib = binding.lib()
+    lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    arrs = [(ctypes.c_void_p * 5)(*[e.value for e in step]) for step in evs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ly = layers[i % len(layers)]
+        lib.moe_workspace_set_stage_events(ly.handle, arrs[i])
+        ly.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for ly in layers:
+        lib.moe_workspace_set_stage_events(ly.handle, None)
+    per_stage = {s: [] for s in stages}
+    for step in evs:
+        for j, s in enumerate(stages):
+            per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
+    mean_ms = {s: float(np.mean(v)) for s, v in per_stage.items()}
+    for step in evs:
+        for e in step:
+            hip.destroy(e)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = T * args.steps / (t1 - t0)
+
+    dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
+    mfma_bound = layer_flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > layer_bytes / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = stage_flops[dominant] / (mean_ms[dominant] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": dominant}
+    else:
+        achieved = stage_bytes[dominant] / (mean_ms[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dominant}
+    layer_time_s = ms_per_step * 1e-3
+    layer_roof = {
+        "bytes": layer_bytes, "flops": layer_flops,
+        "hbm_frac": layer_bytes / layer_time_s / (HBM_PEAK_GBS * 1e9),
+        "mfma_frac": layer_flops / layer_time_s / (MFMA_F16_PEAK_TFLOPS * 1e12),
+        "stage_ms": mean_ms, "active_experts": active,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, x_bits, T, H, I, k)
+
+    for ly in layers:
+        ly.close()
+    result = {
+        "metric": "NVFP4 MoE layer tokens/s + % roofline (HBM GB/s decode, MFMA prefill)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 + e4m3 block-16 + f32 global) operands, f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
+        "config": {"workload": f"nvfp4_moe_layer_{L.name}", "layer_id": args.layer, "T": T, "H": H,
+                   "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
+                   "weights_rotated": args.rotate, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer_roofline": layer_roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, x_bits, T, H, I, k):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from nvfp4_token_quant_amd import synth
+    from tests.layer_fixtures import oracle_weights
+
+    ids, w = oracle.router(synth.router_logits(args.layer, T), k)
+    rng = np.random.default_rng(0)
+    n = T
+    toks = np.arange(T)
+    # grow the sample until it costs about cpu_budget_s (the oracle is linear in tokens)
+    probe = toks[: max(1, min(T, 4))]
+    qw = oracle_weights(args.layer, np.unique(ids[probe]))
+    t0 = time.perf_counter()
+    oracle.moe_layer(x_bits, ids, w, probe, H, I, qw)
+    t_probe = time.perf_counter() - t0
+    n = int(min(T, max(len(probe), args.cpu_budget_s / max(t_probe / len(probe), 1e-6))))
+    toks = np.sort(rng.choice(T, n, replace=False)) if n < T else toks
+    qw = oracle_weights(args.layer, np.unique(ids[toks]))
+    t0 = time.perf_counter()
+    oracle.moe_layer(x_bits, ids, w, toks, H, I, qw)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {T} tokens of the same layer, full forward in binary64 "
+                      f"({dt:.1f} s; weights prepared before timing)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * nvfp4_moe.h — C-ABI of the MI355X (gfx950) NVFP4 fused-MoE layer with
+ * online per-token activation quantization.
+ *
+ * Sources ("the pages"):
+ *   [P1] prhub summary of sglang PR #28354: the CuTe DSL MoE backend gains
+ *        per-token NVFP4 online quantization and in-place scale reload.
+ *   [P2] prhub report of sglang PR #26696: MoE buffers are sized from the
+ *        configured token ceiling, not from the first forward.
+ *   [P3] prhub summary of sglang PR #36624: the MoE runner's steps (routing,
+ *        expandInputRows, activation, finalize) around the expert GEMM.
+ * NVFP4 here: E2M1 codes (OCP MX v1.0), one E4M3 scale (OFP8 "e4m3fn") per
+ * 16 consecutive elements, and one binary32 global scale per token (per
+ * expert for weights).
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are device pointers (HBM) of the current HIP device;
+ *     the library never copies them to the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it asynchronously; no entry point synchronizes the
+ *     host except moe_workspace_create / _destroy (allocation) and
+ *     moe_workspace_bind_weights (a one-time layout conversion).  The library
+ *     never creates streams ([P3] "Implementation breakdown" item 1: one pool
+ *     per stream is what blew up graph-capture memory).
+ *   - Return value: NVFP4_OK (0) or an nvfp4_status code.  All argument checks
+ *     run on the host before anything is launched; on error nothing is
+ *     enqueued and nvfp4_last_error() describes the failure.
+ *   - Layouts are row-major and dense unless a leading dimension is given.
+ *     Packed codes: byte j of a row holds element 2j in its low nibble and
+ *     element 2j+1 in its high nibble.  Block scales are E4M3 bit patterns,
+ *     one byte per 16 elements, row-major [rows, cols/16].
+ */
+#ifndef NVFP4_MOE_H
+#define NVFP4_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1,      /* null / misaligned pointer, bad dimension */
+  NVFP4_ERR_TOO_MANY_TOKENS = 2,  /* T above the workspace's max_num_tokens */
+  NVFP4_ERR_ALIAS = 3,            /* output overlaps an input */
+  NVFP4_ERR_NO_WEIGHTS = 4,       /* forward before moe_workspace_bind_weights */
+  NVFP4_ERR_METADATA_CHANGED = 5, /* refresh with other dims / addresses */
+  NVFP4_ERR_HIP = 6,              /* HIP runtime or launch error */
+  NVFP4_ERR_OOM = 7               /* device allocation failed */
+} nvfp4_status;
+
+/* Thread-local description of the last error of this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/*
+ * Per-token NVFP4 quantization of a bf16 activation matrix.
+ * [P1] "Feature and motivation" and "Implementation breakdown" item 2: each
+ * token gets a dynamic binary32 global scale, the activations become packed
+ * FP4 codes plus block-16 scales ("Review highlights": vector size 16).
+ * Per row: g = 2688 / max|x| (g = 1 for an all-zero row; +inf clamps to
+ * FLT_MAX); per 16-block b: S_b = E4M3_rne_sat(RN(RN(amax_b * g) / 6)),
+ * r_b = RN(g / value(S_b)) (0 if S_b == 0; +inf saturates to FLT_MAX);
+ * code = E2M1_rne_sat(RN(x * r_b)).
+ * Dequantization: x ~= value(code) * value(S_b) / g.
+ *
+ *   x_dev       bf16 [rows, ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= cols
+ *   rows        >= 0 (0 is a no-op)
+ *   cols        > 0, multiple of 16
+ *   codes_dev   u8 [rows, cols/2], 16-byte aligned   (written)
+ *   scales_dev  u8 [rows, cols/16]                   (written)
+ *   gscale_dev  f32 [rows], 4-byte aligned           (written)
+ * Outputs must not overlap x.  Results are bit-identical to the CPU reading
+ * of the recipe above (round to nearest even, no contraction).
+ */
+int nvfp4_quantize_per_token(const void* x_dev, int64_t rows, int64_t cols, int64_t ld_x,
+                             void* codes_dev, void* scales_dev, float* gscale_dev,
+                             void* stream);
+
+/*
+ * NVFP4 quantization of expert weights with one global scale per expert
+ * (the online weight conversion of [P1] "Feature and motivation"; the
+ * per-expert factors w1_alpha / w2_alpha of [P1] "Source snippets" undo it).
+ * Same recipe as nvfp4_quantize_per_token, with g = 2688 / max|W[e]| over the
+ * whole expert tensor and blocks along the last dimension.
+ *
+ *   w_dev       f32 [experts, rows, cols], 16-byte aligned
+ *   experts, rows >= 1; cols > 0, multiple of 16
+ *   codes_dev   u8 [experts, rows, cols/2], 16-byte aligned (written)
+ *   scales_dev  u8 [experts, rows, cols/16]                  (written)
+ *   gscale_dev  f32 [experts]                                (written)
+ *   scratch_dev f32 [experts] caller-provided temporary (per-expert amax)
+ */
+int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, int64_t cols,
+                           void* codes_dev, void* scales_dev, float* gscale_dev,
+                           float* scratch_dev, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* MoE layer                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* Finalize mode flag.  [P1] "Implementation breakdown" item 1 and "Risks"
+ * item 5: the fused atomic finalize is fast but not deterministic, and
+ * deterministic inference switches it off.  Without this flag the weighted
+ * top-k sum is accumulated with fp32 atomics in arrival order; with it the
+ * k slot outputs are summed in slot order j = 0..k-1 (bit-reproducible). */
+#define MOE_DETERMINISTIC_FINALIZE 0x1u
+
+typedef struct moe_config {
+  int64_t max_num_tokens; /* token ceiling: every buffer is sized from it once */
+  int64_t hidden;         /* H: multiple of 128 */
+  int64_t inter;          /* I: multiple of 128 */
+  int32_t num_experts;    /* E: 1..1024 */
+  int32_t top_k;          /* k: 1..min(16, E) */
+  uint32_t flags;         /* MOE_DETERMINISTIC_FINALIZE or 0 */
+} moe_config;
+
+/* NVFP4 expert weights, device pointers.  w13 rows [0, I) are the gate
+ * projection (w1) and rows [I, 2I) the up projection (w3); act = silu(gate)*up.
+ *   w13_codes  u8 [E, 2I, H/2], 16-byte aligned   w13_scales u8 [E, 2I, H/16]
+ *   w13_gscale f32 [E]                            (per-expert global scale)
+ *   w2_codes   u8 [E, H, I/2],  16-byte aligned   w2_scales  u8 [E, H, I/16]
+ *   w2_gscale  f32 [E]
+ * The dims must equal the workspace's (E, H, I). */
+typedef struct moe_nvfp4_weights {
+  int64_t num_experts, hidden, inter;
+  const void* w13_codes;
+  const void* w13_scales;
+  const float* w13_gscale;
+  const void* w2_codes;
+  const void* w2_scales;
+  const float* w2_gscale;
+} moe_nvfp4_weights;
+
+typedef struct moe_workspace moe_workspace;
+
+/*
+ * Create a workspace: every device buffer of the forward is allocated here,
+ * once, from cfg->max_num_tokens ([P2] "Feature and motivation" and
+ * "Implementation breakdown" items 1-3: sizing from the first forward's batch
+ * crashed later, larger batches; the ceiling comes from configuration).
+ * moe_token_ceiling() computes that ceiling from serving limits.
+ * Synchronizes the device (allocation).  *out receives the handle.
+ */
+int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** out);
+
+/*
+ * Bind expert weights.  Codes are BORROWED: the caller keeps them alive, at
+ * the same address, for the workspace's lifetime (update them in place).
+ * Block scales and global scales are COPIED into library-owned buffers in the
+ * kernels' layout (the *_blockscale_mma analogue of [P1] "Implementation
+ * breakdown" item 3).  May be called once; later scale changes go through
+ * refresh_scales_inplace.  Enqueued on `stream`.
+ */
+int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
+
+/*
+ * Forward of the layer on T tokens:
+ *   quantize x per token -> router top-k -> expandInputRows permutation ->
+ *   grouped GEMM1 (gate+up) with SwiGLU -> per-row re-quantization ->
+ *   grouped GEMM2 -> weighted finalize.
+ * ([P3] "Feature and motivation": routing, expandInputRows, activation and
+ * finalize around the expert GEMM; [P1] "Implementation breakdown" item 2:
+ * quantize per token, then run the experts with the per-token scale.)
+ * Router: the k largest logits (ties to the smaller expert index, slots in
+ * descending order), weights = softmax over the chosen k.
+ *
+ *   x_dev        bf16 [T, H], 16-byte aligned
+ *   logits_dev   f32 [T, E]
+ *   T            0..max_num_tokens (0: no-op; above: NVFP4_ERR_TOO_MANY_TOKENS,
+ *                message "num_tokens (T) exceeds max_num_tokens (M)")
+ *   out_dev      bf16 [T, H], 16-byte aligned; must not overlap x_dev or
+ *                logits_dev (NVFP4_ERR_ALIAS; [P3] "Implementation breakdown"
+ *                item 2: in-place MoE output raced with a reader of the input)
+ * No allocation and no host synchronization: the call can be captured in a
+ * HIP graph.  One stream at a time per workspace.
+ */
+int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_dev, int64_t T,
+                      void* out_dev, void* stream);
+
+/*
+ * Reload of weight scales after the caller updated the codes in place
+ * ([P1] "Implementation breakdown" item 3 and "Source snippets",
+ * refresh_cutedsl_standard_scales_for_weight_update): new block scales and
+ * global scales are copied INTO the existing library buffers, so addresses
+ * captured by a HIP graph stay valid.  `w` must carry the bound dims and the
+ * bound code pointers (or NULL code pointers); any difference returns
+ * NVFP4_ERR_METADATA_CHANGED ("recapture is required") and changes nothing.
+ * Enqueued on `stream`, ordered with forwards on the same stream.
+ */
+int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
+
+/* Free library-owned memory (never the caller's codes).  NULL is a no-op.
+ * Synchronizes the device. */
+int moe_workspace_destroy(moe_workspace* ws);
+
+/*
+ * Token ceiling of one forward from serving limits ([P2] "Source snippets",
+ * cutedsl_moe_max_num_tokens): max(max_prefill, piecewise_max if > 0,
+ * graph_max_bs * (spec_draft_tokens if > 0 else 1)).  piecewise_max = 0
+ * means piecewise graphs are disabled.  Host-only, no device access.
+ */
+int moe_token_ceiling(int64_t max_prefill, int64_t piecewise_max, int64_t graph_max_bs,
+                      int64_t spec_draft_tokens, int64_t* out);
+
+/*
+ * Read-only access to the workspace's intermediate buffers (for tests and
+ * inspection).  Returns the device pointer and byte size of one buffer;
+ * contents are those of the last forward on the workspace.
+ *   MOE_BUF_XQ_CODES  u8 [T, H/2]     MOE_BUF_XQ_SCALES u8 [T, H/16]
+ *   MOE_BUF_XQ_GSCALE f32 [T]         MOE_BUF_TOPK_IDS  i32 [T, k]
+ *   MOE_BUF_TOPK_W    f32 [T, k]      MOE_BUF_COUNTS    i32 [E]
+ *   MOE_BUF_OFFSETS   i32 [E + 1]     MOE_BUF_PERM      i32 [T*k] (row -> t*k+j)
+ *   MOE_BUF_INV       i32 [T*k]       ((t*k+j) -> row)
+ *   MOE_BUF_ACT       f32 [T*k, I]    SwiGLU output per expanded row
+ *   MOE_BUF_A2_CODES  u8 [T*k, I/2]   MOE_BUF_A2_SCALES u8 [T*k, I/16]
+ *   MOE_BUF_A2_GSCALE f32 [T*k]       re-quantized activation
+ * (sizes are reported for max_num_tokens rows)
+ */
+typedef enum moe_buffer_id {
+  MOE_BUF_XQ_CODES = 0,
+  MOE_BUF_XQ_SCALES,
+  MOE_BUF_XQ_GSCALE,
+  MOE_BUF_TOPK_IDS,
+  MOE_BUF_TOPK_W,
+  MOE_BUF_COUNTS,
+  MOE_BUF_OFFSETS,
+  MOE_BUF_PERM,
+  MOE_BUF_INV,
+  MOE_BUF_ACT,
+  MOE_BUF_A2_CODES,
+  MOE_BUF_A2_SCALES,
+  MOE_BUF_A2_GSCALE,
+  MOE_BUF_COUNT_
+} moe_buffer_id;
+
+int moe_workspace_buffer(const moe_workspace* ws, int32_t id, void** ptr_out, int64_t* bytes_out);
+
+/*
+ * Per-stage timing (inspection and benchmarks).  With events != NULL, every
+ * later forward on the workspace records the five caller-owned hipEvent_t
+ * handles events[0..4] on its stream: events[0] before the prologue kernel
+ * (quantize + route + permute), events[1] after it, events[2] after GEMM1 +
+ * SwiGLU, events[3] after GEMM2 (with the fused re-quantization), events[4]
+ * after the finalize.  The handles are copied; pass new ones before each
+ * forward to keep several forwards' timings.  NULL stops recording.
+ */
+int moe_workspace_set_stage_events(moe_workspace* ws, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MOE_H */

@@ -1,0 +1,454 @@
+// C-ABI of the NVFP4 fused-MoE layer: argument checks, the workspace (every
+// buffer allocated once from the configured token ceiling), weight binding,
+// in-place scale refresh and the forward's launch sequence.
+//
+// [P2] (sglang PR #26696 report), "Feature and motivation" and
+// "Implementation breakdown": buffers sized from the first forward's batch
+// crashed later batches ("num_tokens (4073) exceeds max_num_tokens (2048)");
+// the ceiling now comes from configuration.  [P1] (sglang PR #28354 summary),
+// "Implementation breakdown" item 3 and "Source snippets": after a weight
+// reload the scales are copied into the existing tensors so that captured
+// graphs keep valid addresses, and a metadata change is an error.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/nvfp4_moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return NVFP4_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+}  // namespace
+
+struct moe_workspace {
+  moe_config cfg;
+  int device;
+  int64_t max_tiles_cap;
+  int route_blocks_cap;
+  // activation quantization
+  uint8_t* xq_codes;
+  uint8_t* xq_scales;
+  float* xq_g;
+  // routing / permutation
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* loc_rank;
+  int32_t* blk_counts;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  int4* tiles;
+  int32_t* n_tiles;
+  uint32_t* ticket;
+  // intermediates
+  float* act;
+  float* act_amax;
+  uint8_t* a2_codes;
+  uint8_t* a2_scales;
+  float* a2_g;
+  float* y;
+  float* out_acc;
+  // weights
+  bool bound;
+  const uint8_t* w13c;
+  const uint8_t* w2c;
+  uint8_t* w13s;
+  uint8_t* w2s;
+  float* w13g;
+  float* w2g;
+  // optional stage-timing events (caller-owned)
+  bool timing;
+  hipEvent_t events[5];
+};
+
+namespace {
+
+// Every buffer the workspace owns, in one list for allocation and release.
+template <typename F>
+void for_each_buffer(moe_workspace* w, F&& f) {
+  const moe_config& c = w->cfg;
+  const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, k = c.top_k;
+  const int64_t R = T * k;
+  const int64_t n_amax = I / nvfp4::gemm1_cols_per_block();
+  const bool det = (c.flags & MOE_DETERMINISTIC_FINALIZE) != 0;
+  f(reinterpret_cast<void**>(&w->xq_codes), T * H / 2);
+  f(reinterpret_cast<void**>(&w->xq_scales), T * H / 16);
+  f(reinterpret_cast<void**>(&w->xq_g), T * 4);
+  f(reinterpret_cast<void**>(&w->topk_ids), R * 4);
+  f(reinterpret_cast<void**>(&w->topk_w), R * 4);
+  f(reinterpret_cast<void**>(&w->loc_rank), R * 4);
+  f(reinterpret_cast<void**>(&w->blk_counts), static_cast<int64_t>(w->route_blocks_cap) * E * 4);
+  f(reinterpret_cast<void**>(&w->counts), E * 4);
+  f(reinterpret_cast<void**>(&w->offsets), (E + 1) * 4);
+  f(reinterpret_cast<void**>(&w->perm), R * 4);
+  f(reinterpret_cast<void**>(&w->inv), R * 4);
+  f(reinterpret_cast<void**>(&w->tiles), w->max_tiles_cap * 16);
+  f(reinterpret_cast<void**>(&w->n_tiles), 4);
+  f(reinterpret_cast<void**>(&w->ticket), 4);
+  f(reinterpret_cast<void**>(&w->act), R * I * 4);
+  f(reinterpret_cast<void**>(&w->act_amax), R * n_amax * 4);
+  f(reinterpret_cast<void**>(&w->a2_codes), R * I / 2);
+  f(reinterpret_cast<void**>(&w->a2_scales), R * I / 16);
+  f(reinterpret_cast<void**>(&w->a2_g), R * 4);
+  f(reinterpret_cast<void**>(&w->y), det ? R * H * 4 : 0);
+  f(reinterpret_cast<void**>(&w->out_acc), det ? 0 : T * H * 4);
+  f(reinterpret_cast<void**>(&w->w13s), E * 2 * I * H / 16);
+  f(reinterpret_cast<void**>(&w->w2s), E * H * I / 16);
+  f(reinterpret_cast<void**>(&w->w13g), E * 4);
+  f(reinterpret_cast<void**>(&w->w2g), E * 4);
+}
+
+void free_all(moe_workspace* w) {
+  for_each_buffer(w, [](void** p, int64_t) {
+    if (*p) (void)hipFree(*p);
+    *p = nullptr;
+  });
+}
+
+// Rows per M-tile from the average rows per routed expert.
+int pick_mt(int64_t T, const moe_config& c) {
+  const int64_t R = T * c.top_k;
+  const int64_t active = std::min<int64_t>(c.num_experts, R);
+  const int64_t avg = (R + active - 1) / std::max<int64_t>(active, 1);
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  return 64;
+}
+
+int64_t tiles_bound(int64_t R, int64_t E, int mt) { return (R + mt - 1) / mt + std::min(E, R); }
+
+int check_weights_desc(const moe_workspace* ws, const moe_nvfp4_weights* w, bool need_codes) {
+  if (!w) return fail(NVFP4_ERR_INVALID_ARG, "weights descriptor is NULL");
+  const moe_config& c = ws->cfg;
+  if (w->num_experts != c.num_experts || w->hidden != c.hidden || w->inter != c.inter)
+    return fail(NVFP4_ERR_METADATA_CHANGED,
+                "weight dims (E=%lld, H=%lld, I=%lld) differ from the workspace's (E=%d, H=%lld, "
+                "I=%lld); recapture is required",
+                (long long)w->num_experts, (long long)w->hidden, (long long)w->inter, c.num_experts,
+                (long long)c.hidden, (long long)c.inter);
+  if (!w->w13_scales || !w->w2_scales || !w->w13_gscale || !w->w2_gscale)
+    return fail(NVFP4_ERR_INVALID_ARG, "weight scale pointers must be non-NULL");
+  if (!aligned(w->w13_gscale, 4) || !aligned(w->w2_gscale, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "global scale pointers must be 4-byte aligned");
+  if (need_codes) {
+    if (!w->w13_codes || !w->w2_codes)
+      return fail(NVFP4_ERR_INVALID_ARG, "weight code pointers must be non-NULL");
+    if (!aligned(w->w13_codes, 16) || !aligned(w->w2_codes, 16))
+      return fail(NVFP4_ERR_INVALID_ARG, "weight code pointers must be 16-byte aligned");
+  }
+  return NVFP4_OK;
+}
+
+hipError_t copy_scales(moe_workspace* ws, const moe_nvfp4_weights* w, hipStream_t s) {
+  const moe_config& c = ws->cfg;
+  const int64_t E = c.num_experts, H = c.hidden, I = c.inter;
+  hipError_t e = nvfp4::launch_swizzle_scales(static_cast<const uint8_t*>(w->w13_scales), ws->w13s,
+                                              E * 2 * I, H, s);
+  if (e == hipSuccess)
+    e = nvfp4::launch_swizzle_scales(static_cast<const uint8_t*>(w->w2_scales), ws->w2s, E * H, I, s);
+  if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w13_gscale, ws->w13g, E, s);
+  if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w2_gscale, ws->w2g, E, s);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_quantize_per_token(const void* x_dev, int64_t rows, int64_t cols, int64_t ld_x,
+                             void* codes_dev, void* scales_dev, float* gscale_dev, void* stream) {
+  if (rows < 0) return fail(NVFP4_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (cols <= 0 || cols % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "cols must be a positive multiple of 16 (got %lld)", (long long)cols);
+  if (cols > (int64_t(1) << 30)) return fail(NVFP4_ERR_INVALID_ARG, "cols too large");
+  if (ld_x < cols || ld_x % 8 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "ld_x must be >= cols and a multiple of 8 (got %lld)", (long long)ld_x);
+  if (rows == 0) return ok();
+  if (rows > (int64_t(1) << 32)) return fail(NVFP4_ERR_INVALID_ARG, "rows too large");
+  if (!x_dev || !codes_dev || !scales_dev || !gscale_dev)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x_dev, 16) || !aligned(codes_dev, 16) || !aligned(gscale_dev, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "x and codes must be 16-byte aligned, gscale 4-byte aligned");
+  const int64_t xbytes = ((rows - 1) * ld_x + cols) * 2;
+  if (overlap(x_dev, xbytes, codes_dev, rows * cols / 2) ||
+      overlap(x_dev, xbytes, scales_dev, rows * cols / 16) || overlap(x_dev, xbytes, gscale_dev, rows * 4))
+    return fail(NVFP4_ERR_ALIAS, "outputs overlap the input x");
+  hipError_t e = nvfp4::launch_quantize_rows(static_cast<const uint16_t*>(x_dev), rows, cols, ld_x,
+                                             static_cast<uint8_t*>(codes_dev),
+                                             static_cast<uint8_t*>(scales_dev), gscale_dev,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "nvfp4_quantize_per_token launch");
+  return ok();
+}
+
+int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, int64_t cols,
+                           void* codes_dev, void* scales_dev, float* gscale_dev, float* scratch_dev,
+                           void* stream) {
+  if (experts < 1 || experts > 65535 || rows < 1 || cols <= 0 || cols % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG,
+                "need 1 <= experts <= 65535, rows >= 1, cols a positive multiple of 16");
+  if (!w_dev || !codes_dev || !scales_dev || !gscale_dev || !scratch_dev)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(w_dev, 16) || !aligned(codes_dev, 16) || !aligned(gscale_dev, 4) || !aligned(scratch_dev, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "w and codes must be 16-byte aligned");
+  const int64_t n = experts * rows * cols;
+  if (overlap(w_dev, n * 4, codes_dev, n / 2) || overlap(w_dev, n * 4, scales_dev, n / 16))
+    return fail(NVFP4_ERR_ALIAS, "outputs overlap the input");
+  hipError_t e = nvfp4::launch_quantize_experts(w_dev, experts, rows, cols, static_cast<uint8_t*>(codes_dev),
+                                                static_cast<uint8_t*>(scales_dev), gscale_dev,
+                                                reinterpret_cast<uint32_t*>(scratch_dev),
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "nvfp4_quantize_experts launch");
+  return ok();
+}
+
+int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** out) {
+  if (!cfg || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL cfg or out");
+  *out = nullptr;
+  const moe_config c = *cfg;
+  if (c.max_num_tokens < 1 || c.max_num_tokens > (int64_t(1) << 24))
+    return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens must be in [1, 2^24] (got %lld)",
+                (long long)c.max_num_tokens);
+  if (c.hidden < 128 || c.hidden % 128 != 0 || c.hidden > 65536)
+    return fail(NVFP4_ERR_INVALID_ARG, "hidden must be a multiple of 128 in [128, 65536] (got %lld)",
+                (long long)c.hidden);
+  if (c.inter < 128 || c.inter % 128 != 0 || c.inter > 65536)
+    return fail(NVFP4_ERR_INVALID_ARG, "inter must be a multiple of 128 in [128, 65536] (got %lld)",
+                (long long)c.inter);
+  if (c.num_experts < 1 || c.num_experts > nvfp4::kMaxExperts)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_experts must be in [1, %d]", nvfp4::kMaxExperts);
+  if (c.top_k < 1 || c.top_k > nvfp4::kMaxTopK || c.top_k > c.num_experts)
+    return fail(NVFP4_ERR_INVALID_ARG, "top_k must be in [1, min(%d, num_experts)]", nvfp4::kMaxTopK);
+  if ((c.flags & ~MOE_DETERMINISTIC_FINALIZE) != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "unknown flags 0x%x", c.flags);
+  if (c.max_num_tokens * c.top_k > (int64_t(1) << 30))
+    return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * top_k too large");
+  moe_workspace* w = new (std::nothrow) moe_workspace();
+  if (!w) return fail(NVFP4_ERR_OOM, "host allocation failed");
+  std::memset(static_cast<void*>(w), 0, sizeof(*w));
+  w->cfg = c;
+  if (hipGetDevice(&w->device) != hipSuccess) {
+    delete w;
+    return fail(NVFP4_ERR_HIP, "hipGetDevice failed");
+  }
+  const int64_t Rmax = c.max_num_tokens * c.top_k;
+  w->max_tiles_cap = tiles_bound(Rmax, c.num_experts, 16);
+  w->route_blocks_cap = static_cast<int>((c.max_num_tokens + 15) / 16);
+  int status = NVFP4_OK;
+  for_each_buffer(w, [&](void** p, int64_t bytes) {
+    if (status != NVFP4_OK || bytes <= 0) return;
+    hipError_t e = hipMalloc(p, static_cast<size_t>(bytes));
+    if (e != hipSuccess) {
+      *p = nullptr;
+      status = fail(NVFP4_ERR_OOM, "hipMalloc of %lld bytes failed: %s", (long long)bytes,
+                    hipGetErrorString(e));
+    }
+  });
+  if (status != NVFP4_OK) {
+    free_all(w);
+    delete w;
+    return status;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = nvfp4::launch_fill_u32(w->ticket, 1, 0u, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    free_all(w);
+    delete w;
+    return hip_fail(e, "workspace initialization");
+  }
+  *out = w;
+  return ok();
+}
+
+int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream) {
+  if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
+  if (ws->bound) return fail(NVFP4_ERR_INVALID_ARG, "weights already bound; use refresh_scales_inplace");
+  int st = check_weights_desc(ws, w, true);
+  if (st != NVFP4_OK) {
+    if (st == NVFP4_ERR_METADATA_CHANGED) g_last_error = "weight dims do not match the workspace";
+    return st == NVFP4_ERR_METADATA_CHANGED ? NVFP4_ERR_INVALID_ARG : st;
+  }
+  hipError_t e = copy_scales(ws, w, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "scale copy");
+  ws->w13c = static_cast<const uint8_t*>(w->w13_codes);
+  ws->w2c = static_cast<const uint8_t*>(w->w2_codes);
+  ws->bound = true;
+  return ok();
+}
+
+int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream) {
+  if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
+  if (!ws->bound) return fail(NVFP4_ERR_NO_WEIGHTS, "no weights bound; call moe_workspace_bind_weights");
+  int st = check_weights_desc(ws, w, false);
+  if (st != NVFP4_OK) return st;
+  if ((w->w13_codes && w->w13_codes != ws->w13c) || (w->w2_codes && w->w2_codes != ws->w2c))
+    return fail(NVFP4_ERR_METADATA_CHANGED,
+                "weight codes moved to a new address; recapture is required (update them in place)");
+  hipError_t e = copy_scales(ws, w, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "scale refresh");
+  return ok();
+}
+
+int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_dev, int64_t T,
+                      void* out_dev, void* stream) {
+  if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
+  const moe_config& c = ws->cfg;
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (T > c.max_num_tokens)
+    return fail(NVFP4_ERR_TOO_MANY_TOKENS, "num_tokens (%lld) exceeds max_num_tokens (%lld)",
+                (long long)T, (long long)c.max_num_tokens);
+  if (!ws->bound) return fail(NVFP4_ERR_NO_WEIGHTS, "no weights bound; call moe_workspace_bind_weights");
+  if (T == 0) return ok();
+  if (!x_dev || !logits_dev || !out_dev) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x_dev, 16) || !aligned(out_dev, 16) || !aligned(logits_dev, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "x and out must be 16-byte aligned, logits 4-byte aligned");
+  const int64_t H = c.hidden, E = c.num_experts;
+  if (overlap(out_dev, T * H * 2, x_dev, T * H * 2) || overlap(out_dev, T * H * 2, logits_dev, T * E * 4))
+    return fail(NVFP4_ERR_ALIAS, "out overlaps x or the router logits (the layer is not in-place)");
+
+  nvfp4::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.T = static_cast<int>(T);
+  p.H = static_cast<int>(H);
+  p.I = static_cast<int>(c.inter);
+  p.E = static_cast<int>(E);
+  p.k = c.top_k;
+  p.R = static_cast<int>(T * c.top_k);
+  p.mt = pick_mt(T, c);
+  p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
+  p.x = static_cast<const uint16_t*>(x_dev);
+  p.logits = logits_dev;
+  p.out = static_cast<uint16_t*>(out_dev);
+  p.xq_codes = ws->xq_codes;
+  p.xq_scales = ws->xq_scales;
+  p.xq_g = ws->xq_g;
+  p.topk_ids = ws->topk_ids;
+  p.topk_w = ws->topk_w;
+  p.loc_rank = ws->loc_rank;
+  p.blk_counts = ws->blk_counts;
+  p.counts = ws->counts;
+  p.offsets = ws->offsets;
+  p.perm = ws->perm;
+  p.inv = ws->inv;
+  p.tiles = ws->tiles;
+  p.n_tiles = ws->n_tiles;
+  p.ticket = ws->ticket;
+  p.act = ws->act;
+  p.act_amax = ws->act_amax;
+  p.a2_codes = ws->a2_codes;
+  p.a2_scales = ws->a2_scales;
+  p.a2_g = ws->a2_g;
+  p.y = ws->y;
+  p.out_acc = ws->out_acc;
+  p.w13c = ws->w13c;
+  p.w13s = ws->w13s;
+  p.w13g = ws->w13g;
+  p.w2c = ws->w2c;
+  p.w2s = ws->w2s;
+  p.w2g = ws->w2g;
+  const int64_t max_tiles = tiles_bound(p.R, E, p.mt);
+  if (max_tiles > ws->max_tiles_cap) return fail(NVFP4_ERR_INVALID_ARG, "internal: tile bound exceeds capacity");
+  hipError_t e = nvfp4::launch_moe_forward(p, static_cast<int>(max_tiles), static_cast<hipStream_t>(stream),
+                                           ws->timing ? ws->events : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_forward launch");
+  return ok();
+}
+
+int moe_workspace_destroy(moe_workspace* ws) {
+  if (!ws) return ok();
+  (void)hipDeviceSynchronize();
+  free_all(ws);
+  delete ws;
+  return ok();
+}
+
+int moe_token_ceiling(int64_t max_prefill, int64_t piecewise_max, int64_t graph_max_bs,
+                      int64_t spec_draft_tokens, int64_t* out) {
+  if (!out) return fail(NVFP4_ERR_INVALID_ARG, "NULL out");
+  if (max_prefill < 0 || piecewise_max < 0 || graph_max_bs < 0 || spec_draft_tokens < 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "limits must be >= 0");
+  const int64_t per_bs = spec_draft_tokens > 0 ? spec_draft_tokens : 1;
+  int64_t prefill = max_prefill;
+  if (piecewise_max > 0) prefill = std::max(prefill, piecewise_max);
+  *out = std::max(prefill, graph_max_bs * per_bs);
+  return ok();
+}
+
+int moe_workspace_set_stage_events(moe_workspace* ws, void* const* events) {
+  if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
+  if (!events) {
+    ws->timing = false;
+    return ok();
+  }
+  for (int i = 0; i < 5; ++i) {
+    if (!events[i]) return fail(NVFP4_ERR_INVALID_ARG, "event %d is NULL", i);
+    ws->events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  ws->timing = true;
+  return ok();
+}
+
+int moe_workspace_buffer(const moe_workspace* ws, int32_t id, void** ptr_out, int64_t* bytes_out) {
+  if (!ws || !ptr_out || !bytes_out) return fail(NVFP4_ERR_INVALID_ARG, "NULL argument");
+  const moe_config& c = ws->cfg;
+  const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, R = T * c.top_k;
+  void* p = nullptr;
+  int64_t n = 0;
+  switch (id) {
+    case MOE_BUF_XQ_CODES: p = ws->xq_codes; n = T * H / 2; break;
+    case MOE_BUF_XQ_SCALES: p = ws->xq_scales; n = T * H / 16; break;
+    case MOE_BUF_XQ_GSCALE: p = ws->xq_g; n = T * 4; break;
+    case MOE_BUF_TOPK_IDS: p = ws->topk_ids; n = R * 4; break;
+    case MOE_BUF_TOPK_W: p = ws->topk_w; n = R * 4; break;
+    case MOE_BUF_COUNTS: p = ws->counts; n = E * 4; break;
+    case MOE_BUF_OFFSETS: p = ws->offsets; n = (E + 1) * 4; break;
+    case MOE_BUF_PERM: p = ws->perm; n = R * 4; break;
+    case MOE_BUF_INV: p = ws->inv; n = R * 4; break;
+    case MOE_BUF_ACT: p = ws->act; n = R * I * 4; break;
+    case MOE_BUF_A2_CODES: p = ws->a2_codes; n = R * I / 2; break;
+    case MOE_BUF_A2_SCALES: p = ws->a2_scales; n = R * I / 16; break;
+    case MOE_BUF_A2_GSCALE: p = ws->a2_g; n = R * 4; break;
+    default: return fail(NVFP4_ERR_INVALID_ARG, "unknown buffer id %d", id);
+  }
+  *ptr_out = p;
+  *bytes_out = n;
+  return ok();
+}
+
+}  // extern "C"

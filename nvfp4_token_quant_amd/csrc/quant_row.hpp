@@ -1,0 +1,86 @@
+// Per-row NVFP4 quantization by one wave (shared by the standalone quantize
+// kernel and the MoE forward's prologue).
+#pragma once
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+__device__ __forceinline__ void unpack16(const uint4& a, const uint4& b, float* f) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+__device__ __forceinline__ float amax16_bf16(const uint4& a, const uint4& b) {
+  // |x| of finite bf16 values orders like the integer (bits & 0x7FFF)
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m = max(m, w[i] & 0x7FFFu);
+    m = max(m, (w[i] >> 16) & 0x7FFFu);
+  }
+  return __uint_as_float(m << 16);
+}
+
+template <int NB>
+__device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
+                                  uint8_t* __restrict__ crow, uint8_t* __restrict__ srow,
+                                  float* __restrict__ gout, int lane) {
+  if constexpr (NB > 0) {
+    uint4 v[NB][2];
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int b = lane + kWave * i;
+      if (b < nblk) {
+        const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
+        v[i][0] = load_stream16(p);
+        v[i][1] = load_stream16(p + 1);
+      } else {
+        v[i][0] = make_uint4(0, 0, 0, 0);
+        v[i][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) am = fmaxf(am, amax16_bf16(v[i][0], v[i][1]));
+    const float g = global_scale(wave_max(am));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int b = lane + kWave * i;
+      if (b < nblk) {
+        float f[16];
+        unpack16(v[i][0], v[i][1], f);
+        uint32_t lo, hi;
+        const uint32_t sb = quantize_block16(f, g, lo, hi);
+        *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
+        srow[b] = static_cast<uint8_t>(sb);
+      }
+    }
+    if (lane == 0) *gout = g;
+  } else {
+    // Rows too long for the register cache: amax pass, then quantize pass.
+    float am = 0.0f;
+    for (int b = lane; b < nblk; b += kWave) {
+      const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
+      am = fmaxf(am, amax16_bf16(p[0], p[1]));
+    }
+    const float g = global_scale(wave_max(am));
+    for (int b = lane; b < nblk; b += kWave) {
+      const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
+      float f[16];
+      unpack16(p[0], p[1], f);
+      uint32_t lo, hi;
+      const uint32_t sb = quantize_block16(f, g, lo, hi);
+      *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
+      srow[b] = static_cast<uint8_t>(sb);
+    }
+    if (lane == 0) *gout = g;
+  }
+}
+
+}  // namespace nvfp4

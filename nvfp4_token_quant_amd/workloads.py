@@ -1,0 +1,43 @@
+"""Device-side preparation of the seeded layers (for benchmarks and tests).
+
+Expert weights are drawn on the device by the counter-based generator
+(libnvfp4synth) and quantized by the library's per-expert quantizer.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding, synth
+
+
+def gpu_weights(layer_id: int, device="cuda", chunk: int = 16):
+    """NVFP4 weights of every expert, generated and quantized on the device."""
+    import torch
+
+    L = synth.LAYERS[layer_id]
+    (r13, c13), (r2, c2) = synth.weight_shapes(layer_id)
+    k13 = synth.weight_key(layer_id, synth.WEIGHT_W13)
+    k2 = synth.weight_key(layer_id, synth.WEIGHT_W2)
+    out = []
+    for key, (r, c) in ((k13, (r13, c13)), (k2, (r2, c2))):
+        codes = torch.empty((L.E, r, c // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((L.E, r, c // 16), dtype=torch.uint8, device=device)
+        g = torch.empty((L.E,), dtype=torch.float32, device=device)
+        for e0 in range(0, L.E, chunk):
+            n = min(chunk, L.E - e0)
+            w = binding.synth_weights(*key, e0, n, (r, c), L.sigma, device=device)
+            qc, qs, qg = binding.quantize_experts(w)
+            codes[e0:e0 + n].copy_(qc)
+            scales[e0:e0 + n].copy_(qs)
+            g[e0:e0 + n].copy_(qg)
+            del w, qc, qs, qg
+        out += [codes, scales, g]
+    torch.cuda.synchronize()
+    return binding.NvFp4Weights(*out)
+
+
+def to_device_bf16(x_bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+

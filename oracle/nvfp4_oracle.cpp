@@ -127,7 +127,9 @@ ORC_API double orc_e4m3_value(uint8_t b) { return e4m3_value(b); }
 //   a   = max |x|                                   (row, or whole tensor)
 //   g   = 448*6 / a  (a > 0; +inf clamps to FLT_MAX), g = 1 for a == 0
 //   per 16-block b:  s_b = RN(RN(amax_b * g) / 6),  S_b = E4M3(s_b),
-//                    d_b = value(S_b),  r_b = d_b > 0 ? RN(g / d_b) : 0
+//                    d_b = value(S_b),  r_b = d_b > 0 ? RN(g / d_b) : 0,
+//                    +inf saturating to FLT_MAX (READING: with g clamped, g / d_b
+//                    can overflow, and inf * 0 would make zeros NaN)
 //   per element:     c_k = E2M1(RN(x_k * r_b))
 //   packing: byte j holds element 2j in the low nibble, 2j+1 in the high one.
 // Dequantization: x^_k = value(c_k) * d_b / g (binary64).
@@ -154,6 +156,7 @@ void quantize_with_g(const float* x, int64_t K, float g, uint8_t* codes, uint8_t
     S[b] = sb;
     float d = static_cast<float>(e4m3_value(sb));  // exact: E4M3 values are binary32 values
     float r = d > 0.0f ? g / d : 0.0f;
+    if (std::isinf(r)) r = FLT_MAX;
     for (int i = 0; i < 16; i += 2) {
       float v0 = xb[i] * r;
       float v1 = xb[i + 1] * r;

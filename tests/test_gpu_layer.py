@@ -1,0 +1,264 @@
+"""GPU parity of the NVFP4 MoE layer against the CPU oracle.
+
+Bit-exact: the per-token quantization inside the forward, router ids, the
+per-expert counts / offsets, the expandInputRows permutation (deterministic
+mode), the re-quantization of the SwiGLU output (Q(act_gpu) == A2_gpu), and
+run-to-run / token-permutation reproducibility in deterministic mode.
+Tolerance: router weights |w - w_ref| <= 2e-6; layer output
+||gpu - ref|| / ||ref|| <= 5e-3 and max |gpu - ref| <= 3e-2 * rms(ref).
+Full-size layers whose oracle would take minutes are checked on sampled
+tokens (every integer output is still checked on every token).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nvfp4_token_quant_amd import binding, synth
+from tests.layer_fixtures import (bf16_tensor_to_f64, check_layer_tolerance, gpu_weights,
+                                  oracle_weights, to_device_bf16)
+
+pytestmark = pytest.mark.gpu
+
+_WEIGHTS = {}
+
+
+def _weights(layer_id):
+    if layer_id not in _WEIGHTS:
+        _WEIGHTS.clear()
+        torch.cuda.empty_cache()
+        _WEIGHTS[layer_id] = gpu_weights(layer_id)
+    return _WEIGHTS[layer_id]
+
+
+def _layer(layer_id, deterministic=True, max_tokens=None):
+    L = synth.LAYERS[layer_id]
+    layer = binding.MoeLayer(max_tokens or L.max_tokens, L.H, L.I, L.E, L.k, deterministic)
+    layer.bind(_weights(layer_id))
+    return layer
+
+
+def _run(layer, x_bits, logits):
+    out = layer.forward(to_device_bf16(x_bits), torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_integer_path(layer, layer_id, x_bits, logits, T):
+    L = synth.LAYERS[layer_id]
+    H, E, k = L.H, L.E, L.k
+    # per-token quantization inside the forward
+    xc = layer.read_buffer("XQ_CODES", torch.uint8, (T, H // 2)).cpu().numpy()
+    xs = layer.read_buffer("XQ_SCALES", torch.uint8, (T, H // 16)).cpu().numpy()
+    xg = layer.read_buffer("XQ_GSCALE", torch.float32, (T,)).cpu().numpy()
+    oc, os_, og = oracle.quantize_rows(x_bits)
+    np.testing.assert_array_equal(xg, og)
+    np.testing.assert_array_equal(xs, os_)
+    np.testing.assert_array_equal(xc, oc)
+    # router
+    ids = layer.read_buffer("TOPK_IDS", torch.int32, (T, k)).cpu().numpy()
+    w = layer.read_buffer("TOPK_W", torch.float32, (T, k)).cpu().numpy()
+    oids, ow = oracle.router(logits, k)
+    np.testing.assert_array_equal(ids, oids)
+    np.testing.assert_allclose(w, ow, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+    # expandInputRows
+    counts, offsets, perm, inv = oracle.permute(oids, E)
+    np.testing.assert_array_equal(layer.read_buffer("COUNTS", torch.int32, (E,)).cpu().numpy(), counts)
+    np.testing.assert_array_equal(layer.read_buffer("OFFSETS", torch.int32, (E + 1,)).cpu().numpy(), offsets)
+    np.testing.assert_array_equal(layer.read_buffer("PERM", torch.int32, (T * k,)).cpu().numpy(), perm)
+    np.testing.assert_array_equal(layer.read_buffer("INV", torch.int32, (T * k,)).cpu().numpy(), inv)
+    return oids, ow, perm
+
+
+def _check_requant(layer, layer_id, T, rows=None):
+    L = synth.LAYERS[layer_id]
+    R, I = T * L.k, L.I
+    act = layer.read_buffer("ACT", torch.float32, (R, I)).cpu().numpy()
+    a2c = layer.read_buffer("A2_CODES", torch.uint8, (R, I // 2)).cpu().numpy()
+    a2s = layer.read_buffer("A2_SCALES", torch.uint8, (R, I // 16)).cpu().numpy()
+    a2g = layer.read_buffer("A2_GSCALE", torch.float32, (R,)).cpu().numpy()
+    rows = np.arange(R) if rows is None else rows
+    c, s, g = oracle.quantize_rows(act[rows])
+    np.testing.assert_array_equal(a2g[rows], g)
+    np.testing.assert_array_equal(a2s[rows], s)
+    np.testing.assert_array_equal(a2c[rows], c)
+    return act
+
+
+def _oracle_out(layer_id, x_bits, ids, w, tokens, debug=False):
+    L = synth.LAYERS[layer_id]
+    experts = np.unique(ids[tokens])
+    qw = oracle_weights(layer_id, experts)
+    return oracle.moe_layer(x_bits, ids, w, tokens, L.H, L.I, qw, debug=debug)
+
+
+@pytest.mark.parametrize("layer_id", [1, 2])
+def test_layer_full(layer_id):
+    L = synth.LAYERS[layer_id]
+    print(f"layer {layer_id} T={L.T}", flush=True)
+    x, logits = synth.activations(layer_id), synth.router_logits(layer_id)
+    layer = _layer(layer_id)
+    out = _run(layer, x, logits)
+    ids, w, perm = _check_integer_path(layer, layer_id, x, logits, L.T)
+    act = _check_requant(layer, layer_id, L.T)
+    toks = np.arange(L.T)
+    ref, dbg = _oracle_out(layer_id, x, ids, w, toks, debug=True)
+    # SwiGLU output per expanded row (fp32 accumulation vs binary64)
+    ref_act = dbg["act"].reshape(L.T * L.k, L.I)[perm]
+    scale = np.abs(ref_act).max(axis=1, keepdims=True)
+    assert np.abs(act - ref_act).max() <= 1e-4 * scale.max()
+    check_layer_tolerance(bf16_tensor_to_f64(out), ref)
+    layer.close()
+
+
+@pytest.mark.timeout(900)
+def test_layer3_prefill_sampled():
+    L = synth.LAYERS[3]
+    print(f"layer 3 T={L.T}", flush=True)
+    x, logits = synth.activations(3), synth.router_logits(3)
+    layer = _layer(3)
+    out = _run(layer, x, logits)
+    ids, w, perm = _check_integer_path(layer, 3, x, logits, L.T)
+    rng = np.random.default_rng(1)
+    _check_requant(layer, 3, L.T, rows=np.sort(rng.choice(L.T * L.k, 2000, replace=False)))
+    toks = np.sort(rng.choice(L.T, 48, replace=False))
+    ref = _oracle_out(3, x, ids, w, toks)
+    check_layer_tolerance(bf16_tensor_to_f64(out)[toks], ref)
+    layer.close()
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("T", [1, 7, 2048])
+def test_layer5_large(T):
+    L = synth.LAYERS[5]
+    print(f"layer 5 T={T} (ceiling {L.max_tokens})", flush=True)
+    x, logits = synth.activations(5, T), synth.router_logits(5, T)
+    layer = _layer(5)
+    out = _run(layer, x, logits)
+    ids, w, _ = _check_integer_path(layer, 5, x, logits, T)
+    counts = layer.read_buffer("COUNTS", torch.int32, (L.E,)).cpu().numpy()
+    assert np.all(counts[synth.cold_experts(5)] == 0)
+    toks = np.arange(T) if T <= 7 else np.array([0, 777, 1500, T - 1])
+    ref = _oracle_out(5, x, ids, w, toks)
+    check_layer_tolerance(bf16_tensor_to_f64(out)[toks], ref)
+    layer.close()
+
+
+def test_deterministic_reproducible_and_permutation_invariant():
+    L = synth.LAYERS[2]
+    x, logits = synth.activations(2), synth.router_logits(2)
+    layer = _layer(2)
+    a = _run(layer, x, logits).clone()
+    b = _run(layer, x, logits).clone()
+    assert torch.equal(a, b)
+    p = np.random.default_rng(4).permutation(L.T)
+    c = _run(layer, x[p], logits[p])
+    assert torch.equal(c, a[torch.from_numpy(p).cuda()])
+    layer.close()
+
+
+def test_atomic_finalize_within_tolerance():
+    L = synth.LAYERS[2]
+    x, logits = synth.activations(2), synth.router_logits(2)
+    det = _layer(2)
+    ref_gpu = bf16_tensor_to_f64(_run(det, x, logits))
+    det.close()
+    fast = _layer(2, deterministic=False)
+    out = bf16_tensor_to_f64(_run(fast, x, logits))
+    ids, w = oracle.router(logits, L.k)
+    ref = _oracle_out(2, x, ids, w, np.arange(L.T))
+    check_layer_tolerance(out, ref)
+    # same math in another summation order: within a few bf16 ulps of the slot-ordered sum
+    assert np.abs(out - ref_gpu).max() <= 4 * 2.0 ** -8 * np.abs(ref_gpu).max()
+    fast.close()
+
+
+def test_ragged_token_counts_share_one_workspace():
+    """One workspace sized for 64 tokens, forwards at T = 64, 1, 13, 0, 64."""
+    L = synth.LAYERS[2]
+    x, logits = synth.activations(2), synth.router_logits(2)
+    layer = _layer(2)
+    full = bf16_tensor_to_f64(_run(layer, x, logits))
+    for T in (1, 13):
+        out = bf16_tensor_to_f64(_run(layer, x[:T], logits[:T]))
+        np.testing.assert_array_equal(out, full[:T])
+    empty = torch.empty((0, L.H), dtype=torch.bfloat16, device="cuda")
+    layer.forward_into(empty, torch.empty((0, L.E), device="cuda"), empty, T=0)
+    np.testing.assert_array_equal(bf16_tensor_to_f64(_run(layer, x, logits)), full)
+    layer.close()
+
+
+def test_graph_capture_and_inplace_scale_refresh():
+    """A captured forward keeps working after refresh_scales_inplace: its
+    replay equals an eager forward with the new scales, bit for bit."""
+    L = synth.LAYERS[2]
+    x = to_device_bf16(synth.activations(2))
+    logits = torch.from_numpy(synth.router_logits(2)).cuda()
+    wts = _weights(2)
+    layer = binding.MoeLayer(L.T, L.H, L.I, L.E, L.k, True)
+    mine = binding.NvFp4Weights(wts.w13_codes, wts.w13_scales.clone(), wts.w13_gscale.clone(),
+                                wts.w2_codes, wts.w2_scales.clone(), wts.w2_gscale.clone())
+    layer.bind(mine)
+    out = torch.empty_like(x)
+    layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward_into(x, logits, out)   # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    # reload: w2 global scales doubled -> every y halves exactly -> out halves
+    mine.w2_gscale.mul_(2.0)
+    layer.refresh_scales(mine)
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = out.clone()
+    fresh = torch.empty_like(x)
+    layer.forward_into(x, logits, fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(replayed, fresh)
+    assert torch.equal(replayed.float() * 2, eager.float())
+    # metadata changes are refused
+    bad = binding.NvFp4Weights(wts.w13_codes.clone(), mine.w13_scales, mine.w13_gscale,
+                               wts.w2_codes, mine.w2_scales, mine.w2_gscale)
+    with pytest.raises(binding.Nvfp4Error) as ei:
+        layer.refresh_scales(bad)
+    assert ei.value.status == "NVFP4_ERR_METADATA_CHANGED"
+    layer.close()
+
+
+def test_error_paths():
+    L = synth.LAYERS[2]
+    layer = binding.MoeLayer(L.T, L.H, L.I, L.E, L.k, True)
+    x = to_device_bf16(synth.activations(2))
+    logits = torch.from_numpy(synth.router_logits(2)).cuda()
+    with pytest.raises(binding.Nvfp4Error) as ei:
+        layer.forward(x, logits)
+    assert ei.value.status == "NVFP4_ERR_NO_WEIGHTS"
+    layer.bind(_weights(2))
+    x65 = torch.cat([x, x[:1]])
+    l65 = torch.cat([logits, logits[:1]])
+    with pytest.raises(binding.Nvfp4Error) as ei:
+        layer.forward(x65, l65)
+    assert ei.value.status == "NVFP4_ERR_TOO_MANY_TOKENS"
+    assert "num_tokens (65) exceeds max_num_tokens (64)" in str(ei.value)
+    with pytest.raises(binding.Nvfp4Error) as ei:
+        layer.forward_into(x, logits, x)
+    assert ei.value.status == "NVFP4_ERR_ALIAS"
+    layer.close()
+
+
+def test_smoke_entry_point():
+    import __graft_entry__
+    __graft_entry__.smoke()

@@ -81,10 +81,20 @@ def test_row_max_block_gets_448_and_zero_rows():
 
 
 def test_tiny_row_clamps_global_scale():
+    """amax below 2688 / FLT_MAX: g clamps to FLT_MAX, and so does r_b = g / d_b,
+    so zeros stay zero codes instead of becoming NaN (0 * inf)."""
     x = np.zeros((1, 32), np.float32)
     x[0, 3] = np.float32(1e-38)            # 2688 / 1e-38 overflows binary32
+    x[0, 5] = np.float32(-2e-39)
     c, S, g = oracle.quantize_rows(x)
-    assert g[0] == np.finfo(np.float32).max
+    fmax = np.finfo(np.float32).max
+    assert g[0] == fmax
+    # block 0: s = RN(RN(1e-38 * FLT_MAX) / 6) = 0.567 -> E4M3 0.5625 (0x31);
+    # r = FLT_MAX / 0.5625 overflows -> FLT_MAX; x * r = 3.4028 -> 3 (code 5),
+    # -2e-39 * FLT_MAX = -0.68 -> -0.5 (code 0x9), zeros -> +0
+    assert S[0, 0] == 0x31 and S[0, 1] == 0
+    assert c[0, 1] == 0x50 and c[0, 2] == 0x90
+    assert not np.delete(c[0], [1, 2]).any()
 
 
 def _bound_check(x, c, S, g):
