@@ -18,8 +18,7 @@
  *     the library never copies them to the host.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it asynchronously; no entry point synchronizes the
- *     host except moe_workspace_create / _destroy (allocation) and
- *     moe_workspace_bind_weights (a one-time layout conversion).  The library
+ *     host except moe_workspace_create / _destroy (allocation).  The library
  *     never creates streams ([P3] "Implementation breakdown" item 1: one pool
  *     per stream is what blew up graph-capture memory).
  *   - Return value: NVFP4_OK (0) or an nvfp4_status code.  All argument checks
@@ -145,12 +144,14 @@ typedef struct moe_workspace moe_workspace;
 int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** out);
 
 /*
- * Bind expert weights.  Codes are BORROWED: the caller keeps them alive, at
- * the same address, for the workspace's lifetime (update them in place).
- * Block scales and global scales are COPIED into library-owned buffers in the
- * kernels' layout (the *_blockscale_mma analogue of [P1] "Implementation
- * breakdown" item 3).  May be called once; later scale changes go through
- * refresh_scales_inplace.  Enqueued on `stream`.
+ * Bind expert weights.  Codes, block scales and global scales are COPIED
+ * into library-owned buffers in the kernels' fragment-major layout (the
+ * *_blockscale_mma analogue of [P1] "Implementation breakdown" item 3; one
+ * wave load then reads 1 KB of contiguous memory).  The caller's code
+ * addresses are remembered: a later refresh_scales_inplace re-reads the
+ * codes from the same addresses (weights reloaded in place).  May be called
+ * once per workspace.  Enqueued on `stream`; the caller's buffers must stay
+ * valid until that work has run.
  */
 int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
 
@@ -179,12 +180,13 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
                       void* out_dev, void* stream);
 
 /*
- * Reload of weight scales after the caller updated the codes in place
- * ([P1] "Implementation breakdown" item 3 and "Source snippets",
- * refresh_cutedsl_standard_scales_for_weight_update): new block scales and
- * global scales are copied INTO the existing library buffers, so addresses
- * captured by a HIP graph stay valid.  `w` must carry the bound dims and the
- * bound code pointers (or NULL code pointers); any difference returns
+ * Reload after the caller updated the weights in place ([P1]
+ * "Implementation breakdown" item 3 and "Source snippets",
+ * refresh_cutedsl_standard_scales_for_weight_update): the codes (re-read
+ * from the bound addresses), the new block scales and the global scales are
+ * copied INTO the existing library buffers, so addresses captured by a HIP
+ * graph stay valid.  `w` must carry the bound dims and the bound code
+ * pointers (or NULL code pointers); any difference returns
  * NVFP4_ERR_METADATA_CHANGED ("recapture is required") and changes nothing.
  * Enqueued on `stream`, ordered with forwards on the same stream.
  */

@@ -7,14 +7,50 @@
 
 namespace nvfp4 {
 
-// Tokens handled by one block of the forward's prologue kernel.
-constexpr int kRouteTokensPerBlock = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
+constexpr int kMaxRouteBlocks = 256;       // prologue blocks for T <= 32768
+constexpr int kMaxTokensPerRouteBlock = 128;
+
+// Tokens per prologue block: one token per wave up to 1024 tokens, then as
+// many as keep the block count at kMaxRouteBlocks.
+inline int route_tokens_per_block(int64_t T) {
+  if (T <= 4 * kMaxRouteBlocks) return 4;
+  int64_t tpb = (T + kMaxRouteBlocks - 1) / kMaxRouteBlocks;
+  tpb = (tpb + 3) / 4 * 4;
+  return static_cast<int>(tpb > kMaxTokensPerRouteBlock ? kMaxTokensPerRouteBlock : tpb);
+}
+
+// Expert weights are kept in a fragment-major layout so that one wave load
+// reads 1 KB of contiguous memory.  A weight matrix [N, K] (N % 16 == 0,
+// K % 128 == 0; the experts' matrices stacked along N) is cut into 16-row
+// groups i and 128-wide K steps s:
+//   codes:  block (i, s) = 1 KB at ((i * steps(K) + s) * 1024); lane l of a
+//           wave owns bytes [16 l, 16 l + 16) = row 16 i + l % 16, code bytes
+//           [64 s + 16 (l / 16), + 16) of that row (32 codes, k = 128 s +
+//           32 (l / 16) + 0..31).
+//   scales: block (i, q) = 1 KB at ((i * sgroups(K) + q) * 1024) for steps
+//           8 q .. 8 q + 7; lane l owns 16 bytes: for step 8 q + t the two
+//           E4M3 bytes of blocks 8 s + 2 (l / 16) + {0, 1} of row 16 i + l % 16
+//           at bytes 2 t, 2 t + 1 (zero past the last step).
+__host__ __device__ constexpr int ksteps(int K) { return K / 128; }
+__host__ __device__ constexpr int sgroups(int K) { return (K / 128 + 7) / 8; }
+__host__ __device__ constexpr int64_t packed_scale_bytes(int64_t rows, int K) {
+  return rows / 16 * sgroups(K) * 1024;
+}
+
+// Grouped-GEMM kernel families.
+//   stream: tiles of up to 16*fm rows (fm = 1, 2); the whole token operand of
+//           the tile is staged once in LDS as FP4 codes + scales, and each
+//           wave streams its weight rows with a 4-step register prefetch.
+//   tiled:  64-row tiles; token operand staged in K chunks as fp16.
+enum GemmKind { kGemmStream = 0, kGemmTiled = 1 };
 
 struct FwdParams {
   int T, H, I, E, k, R;
   int mt;             // rows per M-tile of the grouped GEMMs
+  int gemm_kind;      // GemmKind
+  int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
   // caller tensors
   const uint16_t* x;
@@ -38,13 +74,13 @@ struct FwdParams {
   uint32_t* ticket;     // device scalar, 0 between launches
   // intermediates
   float* act;       // [R, I]
-  float* act_amax;  // [R, I / g1_cols]
+  float* act_amax;  // [R, I / 64] partial row amax per GEMM1 column band
   uint8_t* a2_codes;
   uint8_t* a2_scales;
   float* a2_g;
   float* y;        // [R, H] (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
-  // weights: codes borrowed, scales in the kernels' layout (see swizzle)
+  // weights, fragment-major copies (see ksteps / sgroups)
   const uint8_t* w13c;
   const uint8_t* w13s;
   const float* w13g;
@@ -61,15 +97,24 @@ hipError_t launch_quantize_experts(const float* w, int64_t experts, int64_t rows
                                    uint8_t* codes, uint8_t* scales, float* gs, uint32_t* amax_bits,
                                    hipStream_t s);
 
+// gemm_kernels.hip
+// Rows per tile and kernel family for a forward of T tokens.
+void choose_gemm(int64_t T, int H, int I, int E, int k, int* mt, int* kind, int* g1_bands);
+// Dynamic LDS bytes of the stream kernel for reduction length K.
+int stream_lds_bytes(int fm, int K);
+hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s,
+                                hipEvent_t const* events);
+
 // moe_kernels.hip
-// Columns of the gate/up output (act columns) one GEMM1 block covers.
-int gemm1_cols_per_block();
 // events: NULL or 5 events recorded around the four kernels.
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* events);
-// Copy [groups*rows, K/16] row-major E4M3 scales into the GEMM layout.
-hipError_t launch_swizzle_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                                 hipStream_t s);
+// Copy row-major codes [rows, K/2] / scales [rows, K/16] into the
+// fragment-major layout (rows % 16 == 0, K % 128 == 0).
+hipError_t launch_pack_codes(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                             hipStream_t s);
+hipError_t launch_pack_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                              hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 

@@ -83,8 +83,10 @@ struct moe_workspace {
   float* out_acc;
   // weights
   bool bound;
-  const uint8_t* w13c;
-  const uint8_t* w2c;
+  const void* bound_w13c;  // caller's code pointers at bind time
+  const void* bound_w2c;
+  uint8_t* w13c;  // fragment-major copies
+  uint8_t* w2c;
   uint8_t* w13s;
   uint8_t* w2s;
   float* w13g;
@@ -102,7 +104,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   const moe_config& c = w->cfg;
   const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, k = c.top_k;
   const int64_t R = T * k;
-  const int64_t n_amax = I / nvfp4::gemm1_cols_per_block();
+  const int64_t n_amax = I / 64;  // GEMM1 column bands of 64 (the finest band used)
   const bool det = (c.flags & MOE_DETERMINISTIC_FINALIZE) != 0;
   f(reinterpret_cast<void**>(&w->xq_codes), T * H / 2);
   f(reinterpret_cast<void**>(&w->xq_scales), T * H / 16);
@@ -125,8 +127,10 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->a2_g), R * 4);
   f(reinterpret_cast<void**>(&w->y), det ? R * H * 4 : 0);
   f(reinterpret_cast<void**>(&w->out_acc), det ? 0 : T * H * 4);
-  f(reinterpret_cast<void**>(&w->w13s), E * 2 * I * H / 16);
-  f(reinterpret_cast<void**>(&w->w2s), E * H * I / 16);
+  f(reinterpret_cast<void**>(&w->w13c), E * 2 * I * H / 2);
+  f(reinterpret_cast<void**>(&w->w2c), E * H * I / 2);
+  f(reinterpret_cast<void**>(&w->w13s), nvfp4::packed_scale_bytes(E * 2 * I, static_cast<int>(H)));
+  f(reinterpret_cast<void**>(&w->w2s), nvfp4::packed_scale_bytes(E * H, static_cast<int>(I)));
   f(reinterpret_cast<void**>(&w->w13g), E * 4);
   f(reinterpret_cast<void**>(&w->w2g), E * 4);
 }
@@ -136,16 +140,6 @@ void free_all(moe_workspace* w) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
   });
-}
-
-// Rows per M-tile from the average rows per routed expert.
-int pick_mt(int64_t T, const moe_config& c) {
-  const int64_t R = T * c.top_k;
-  const int64_t active = std::min<int64_t>(c.num_experts, R);
-  const int64_t avg = (R + active - 1) / std::max<int64_t>(active, 1);
-  if (avg <= 16) return 16;
-  if (avg <= 32) return 32;
-  return 64;
 }
 
 int64_t tiles_bound(int64_t R, int64_t E, int mt) { return (R + mt - 1) / mt + std::min(E, R); }
@@ -172,13 +166,18 @@ int check_weights_desc(const moe_workspace* ws, const moe_nvfp4_weights* w, bool
   return NVFP4_OK;
 }
 
-hipError_t copy_scales(moe_workspace* ws, const moe_nvfp4_weights* w, hipStream_t s) {
+// Copy codes and scales into the library's fragment-major buffers (same
+// addresses on every call) and the global scales into their own buffers.
+hipError_t copy_weights(moe_workspace* ws, const moe_nvfp4_weights* w, const void* w13c,
+                        const void* w2c, hipStream_t s) {
   const moe_config& c = ws->cfg;
   const int64_t E = c.num_experts, H = c.hidden, I = c.inter;
-  hipError_t e = nvfp4::launch_swizzle_scales(static_cast<const uint8_t*>(w->w13_scales), ws->w13s,
-                                              E * 2 * I, H, s);
+  hipError_t e = nvfp4::launch_pack_codes(static_cast<const uint8_t*>(w13c), ws->w13c, E * 2 * I, H, s);
+  if (e == hipSuccess) e = nvfp4::launch_pack_codes(static_cast<const uint8_t*>(w2c), ws->w2c, E * H, I, s);
   if (e == hipSuccess)
-    e = nvfp4::launch_swizzle_scales(static_cast<const uint8_t*>(w->w2_scales), ws->w2s, E * H, I, s);
+    e = nvfp4::launch_pack_scales(static_cast<const uint8_t*>(w->w13_scales), ws->w13s, E * 2 * I, H, s);
+  if (e == hipSuccess)
+    e = nvfp4::launch_pack_scales(static_cast<const uint8_t*>(w->w2_scales), ws->w2s, E * H, I, s);
   if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w13_gscale, ws->w13g, E, s);
   if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w2_gscale, ws->w2g, E, s);
   return e;
@@ -268,7 +267,9 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
   }
   const int64_t Rmax = c.max_num_tokens * c.top_k;
   w->max_tiles_cap = tiles_bound(Rmax, c.num_experts, 16);
-  w->route_blocks_cap = static_cast<int>((c.max_num_tokens + 15) / 16);
+  w->route_blocks_cap = static_cast<int>(std::max<int64_t>(
+      nvfp4::kMaxRouteBlocks,
+      (c.max_num_tokens + nvfp4::kMaxTokensPerRouteBlock - 1) / nvfp4::kMaxTokensPerRouteBlock));
   int status = NVFP4_OK;
   for_each_buffer(w, [&](void** p, int64_t bytes) {
     if (status != NVFP4_OK || bytes <= 0) return;
@@ -304,10 +305,10 @@ int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_weights* w, vo
     if (st == NVFP4_ERR_METADATA_CHANGED) g_last_error = "weight dims do not match the workspace";
     return st == NVFP4_ERR_METADATA_CHANGED ? NVFP4_ERR_INVALID_ARG : st;
   }
-  hipError_t e = copy_scales(ws, w, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "scale copy");
-  ws->w13c = static_cast<const uint8_t*>(w->w13_codes);
-  ws->w2c = static_cast<const uint8_t*>(w->w2_codes);
+  hipError_t e = copy_weights(ws, w, w->w13_codes, w->w2_codes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "weight copy");
+  ws->bound_w13c = w->w13_codes;
+  ws->bound_w2c = w->w2_codes;
   ws->bound = true;
   return ok();
 }
@@ -317,11 +318,11 @@ int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* 
   if (!ws->bound) return fail(NVFP4_ERR_NO_WEIGHTS, "no weights bound; call moe_workspace_bind_weights");
   int st = check_weights_desc(ws, w, false);
   if (st != NVFP4_OK) return st;
-  if ((w->w13_codes && w->w13_codes != ws->w13c) || (w->w2_codes && w->w2_codes != ws->w2c))
+  if ((w->w13_codes && w->w13_codes != ws->bound_w13c) || (w->w2_codes && w->w2_codes != ws->bound_w2c))
     return fail(NVFP4_ERR_METADATA_CHANGED,
                 "weight codes moved to a new address; recapture is required (update them in place)");
-  hipError_t e = copy_scales(ws, w, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "scale refresh");
+  hipError_t e = copy_weights(ws, w, ws->bound_w13c, ws->bound_w2c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "weight refresh");
   return ok();
 }
 
@@ -350,7 +351,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.E = static_cast<int>(E);
   p.k = c.top_k;
   p.R = static_cast<int>(T * c.top_k);
-  p.mt = pick_mt(T, c);
+  nvfp4::choose_gemm(T, p.H, p.I, p.E, p.k, &p.mt, &p.gemm_kind, &p.g1_bands);
   p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
   p.x = static_cast<const uint16_t*>(x_dev);
   p.logits = logits_dev;

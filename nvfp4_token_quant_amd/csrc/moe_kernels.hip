@@ -33,10 +33,10 @@ namespace nvfp4 {
 // the k slots (the softmax over all experts restricted to the chosen k).
 // One wave per token; lane l holds experts l, l+64, ...
 // ---------------------------------------------------------------------------
+template <int kPerLane>
 __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
                                  int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                                  int32_t* __restrict__ lds_ids, int lane) {
-  constexpr int kPerLane = kMaxExperts / kWave;
   float v[kPerLane];
   uint32_t avail = 0;
 #pragma unroll
@@ -96,8 +96,6 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
 // expert in ascending (t, j) order, the per-expert offsets and the M-tile list
 // of the grouped GEMMs.
 // ---------------------------------------------------------------------------
-constexpr int kMaxTokensPerBlock = 128;
-
 __device__ void build_schedule_last_block(const FwdParams& p, int nblocks, int tpb) {
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts];
@@ -187,9 +185,9 @@ __device__ void build_schedule_last_block(const FwdParams& p, int nblocks, int t
   if (tid == 0) *p.ticket = 0u;
 }
 
-template <int NB>
+template <int NB, int KPL>
 __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
-  __shared__ int32_t s_ids[kMaxTokensPerBlock * kMaxTopK];
+  __shared__ int32_t s_ids[kMaxTokensPerRouteBlock * kMaxTopK];
   __shared__ int s_last;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int t0 = blockIdx.x * tpb;
@@ -199,8 +197,8 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
     const int64_t t = t0 + lt;
     quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
                           p.xq_g + t, lane);
-    route_token_wave(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
-                     s_ids + lt * k, lane);
+    route_token_wave<KPL>(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
+                          s_ids + lt * k, lane);
     if (!p.deterministic) {
       float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
       for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -226,283 +224,6 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   if (!s_last) return;
   __threadfence();
   build_schedule_last_block(p, gridDim.x, tpb);
-}
-
-// ---------------------------------------------------------------------------
-// Grouped GEMMs.  One block = one M-tile (up to 16*FM rows of one expert)
-// times a band of weight rows; 4 waves, each owning FN fragments of 16 weight
-// rows.  The token operand is staged through LDS as exact fp16 in K chunks of
-// up to kKC elements; the weight operand streams from HBM straight into
-// registers (each weight byte is used by exactly one block per M-tile).
-// ---------------------------------------------------------------------------
-// K chunk staged per LDS pass: 512 elements for tiles of up to 32 rows, 256
-// for 64-row tiles (keeps the staging buffer near 33 KB).
-template <int FM>
-struct Chunk {
-  static constexpr int KC = FM >= 4 ? 256 : 512;
-  static constexpr int pitch = KC + 8;  // fp16 elements per LDS row (16-byte pad)
-};
-
-// Load the 16-byte code piece and the two block-scale bytes of one weight
-// fragment row for one 128-wide K step.  Scales are in the swizzled layout
-// [row][g][step][2] (see swizzle_scales_kernel).
-__device__ __forceinline__ void load_weight_piece(const uint8_t* __restrict__ wc,
-                                                  const uint8_t* __restrict__ ws, int64_t row,
-                                                  int K, int step, int g, uint4& codes,
-                                                  uint32_t& sc) {
-  codes = load_stream16(wc + row * (K / 2) + step * 64 + g * 16);
-  sc = *reinterpret_cast<const uint16_t*>(ws + row * (K / 16) + g * (K / 64) + step * 2);
-}
-
-template <int FM, int FN>
-__device__ __forceinline__ void mma_chunk(const _Float16 (*lds)[Chunk<FM>::pitch], int nsteps,
-                                          const uint4 (&wc)[FN][4], const uint32_t (&wsc)[FN][4],
-                                          f32x4 (&acc)[FN][FM], int g, int r16) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s >= nsteps) break;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      half8 bfrag[FM];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        bfrag[fm] = *reinterpret_cast<const half8*>(&lds[fm * 16 + r16][s * 128 + 32 * g + 8 * q]);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const uint32_t word = q == 0 ? wc[f][s].x : q == 1 ? wc[f][s].y : q == 2 ? wc[f][s].z : wc[f][s].w;
-        const half2v sc2 = e4m3_half2((wsc[f][s] >> (8 * (q >> 1))) & 0xFFu);
-        const half8 afrag = dequant8_f16(word, sc2);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag[fm], acc[f][fm], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// GEMM1: h = x^ . W13[e]^T for act columns [c0, c0 + 64*FNH) of this block
-// (gate rows c and up rows I + c), then act = silu(h_gate) * h_up per
-// expanded row, stored in fp32 with the block's partial row amax.
-template <int FM, int FNH>
-__global__ __launch_bounds__(256) void moe_gemm1_kernel(FwdParams p) {
-  constexpr int MT = 16 * FM;
-  constexpr int FN = 2 * FNH;
-  constexpr int kKC = Chunk<FM>::KC;
-  __shared__ _Float16 lds[MT][Chunk<FM>::pitch];
-  __shared__ int s_tok[MT];
-  __shared__ float s_ginv[MT];
-  __shared__ float s_amax[4][MT];
-  if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
-  const int4 td = p.tiles[blockIdx.x];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const int H = p.H, I = p.I;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int g = lane >> 4, r16 = lane & 15;
-  if (threadIdx.x < MT) {
-    const int m = threadIdx.x;
-    int tok = -1;
-    float gi = 0.0f;
-    if (m < nrows) {
-      tok = p.perm[row0 + m] / p.k;
-      gi = 1.0f / p.xq_g[tok];
-    }
-    s_tok[m] = tok;
-    s_ginv[m] = gi;
-  }
-  const int c0 = blockIdx.y * (4 * 16 * FNH) + wave * 16 * FNH;  // first act column of the wave
-  const uint8_t* wc = p.w13c + static_cast<int64_t>(e) * 2 * I * (H / 2);
-  const uint8_t* ws = p.w13s + static_cast<int64_t>(e) * 2 * I * (H / 16);
-  f32x4 acc[FN][FM];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kc = 0; kc < H; kc += kKC) {
-    const int nsteps = min(kKC, H - kc) / 128;
-    uint4 wcodes[FN][4];
-    uint32_t wsc[FN][4];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t n = (f < FNH) ? (c0 + f * 16 + r16) : (I + c0 + (f - FNH) * 16 + r16);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < nsteps) load_weight_piece(wc, ws, n, H, kc / 128 + s, g, wcodes[f][s], wsc[f][s]);
-    }
-    __syncthreads();
-    // stage the token operand: rows x (nsteps*128) fp16, 32 elements per item
-    const int items = MT * nsteps * 4;
-    for (int it = threadIdx.x; it < items; it += 256) {
-      const int m = it / (nsteps * 4);
-      const int kk = (it % (nsteps * 4)) * 32;
-      const int tok = s_tok[m];
-      half8* dst = reinterpret_cast<half8*>(&lds[m][kk]);
-      if (tok >= 0) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(p.xq_codes + static_cast<int64_t>(tok) * (H / 2) + (kc + kk) / 2);
-        const uint16_t sw = *reinterpret_cast<const uint16_t*>(p.xq_scales + static_cast<int64_t>(tok) * (H / 16) + (kc + kk) / 16);
-        const half2v s0 = e4m3_half2(sw & 0xFFu), s1 = e4m3_half2(sw >> 8);
-        dst[0] = dequant8_f16(cw.x, s0);
-        dst[1] = dequant8_f16(cw.y, s0);
-        dst[2] = dequant8_f16(cw.z, s1);
-        dst[3] = dequant8_f16(cw.w, s1);
-      } else {
-        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        dst[0] = z; dst[1] = z; dst[2] = z; dst[3] = z;
-      }
-    }
-    __syncthreads();
-    mma_chunk<FM, FN>(lds, nsteps, wcodes, wsc, acc, g, r16);
-  }
-
-  // epilogue: lane holds D[n = 4g + i][m = r16] of each fragment
-  const float wginv = 1.0f / p.w13g[e];
-  float am[FM];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    am[fm] = 0.0f;
-    const int m = fm * 16 + r16;
-    const float alpha = s_ginv[m] * wginv;
-#pragma unroll
-    for (int fh = 0; fh < FNH; ++fh) {
-      float a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float hg = acc[fh][fm][i] * alpha;
-        const float hu = acc[FNH + fh][fm][i] * alpha;
-        a[i] = hg / (1.0f + __expf(-hg)) * hu;
-        am[fm] = fmaxf(am[fm], fabsf(a[i]));
-      }
-      if (m < nrows) {
-        const int n = c0 + fh * 16 + 4 * g;
-        *reinterpret_cast<float4*>(p.act + static_cast<int64_t>(row0 + m) * I + n) =
-            make_float4(a[0], a[1], a[2], a[3]);
-      }
-    }
-    am[fm] = fmaxf(am[fm], __shfl_xor(am[fm], 16, kWave));
-    am[fm] = fmaxf(am[fm], __shfl_xor(am[fm], 32, kWave));
-    if (g == 0) s_amax[wave][m] = am[fm];
-  }
-  __syncthreads();
-  if (threadIdx.x < MT && static_cast<int>(threadIdx.x) < nrows) {
-    const int m = threadIdx.x;
-    const float v = fmaxf(fmaxf(s_amax[0][m], s_amax[1][m]), fmaxf(s_amax[2][m], s_amax[3][m]));
-    p.act_amax[static_cast<int64_t>(row0 + m) * gridDim.y + blockIdx.y] = v;
-  }
-}
-
-// GEMM2: y = a^2 . W2[e]^T for output columns [n0, n0 + 64*FN).  The token
-// operand is the per-row re-quantization of act (same recipe as the token
-// quantizer, on fp32 input, with g2 from the row amax), done while staging;
-// the blocks of the first column band also store it (codes, scales, g2).
-template <int FM, int FN>
-__global__ __launch_bounds__(256) void moe_gemm2_kernel(FwdParams p, int n_amax) {
-  constexpr int MT = 16 * FM;
-  constexpr int kKC = Chunk<FM>::KC;
-  __shared__ _Float16 lds[MT][Chunk<FM>::pitch];
-  __shared__ float s_g2[MT];
-  __shared__ int s_slot[MT];
-  if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
-  const int4 td = p.tiles[blockIdx.x];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const int H = p.H, I = p.I;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int g = lane >> 4, r16 = lane & 15;
-  const bool write_a2 = blockIdx.y == 0;
-  if (threadIdx.x < MT) {
-    const int m = threadIdx.x;
-    float g2 = 1.0f;
-    int slot = -1;
-    if (m < nrows) {
-      float a = 0.0f;
-      for (int j = 0; j < n_amax; ++j) a = fmaxf(a, p.act_amax[static_cast<int64_t>(row0 + m) * n_amax + j]);
-      g2 = global_scale(a);
-      slot = p.perm[row0 + m];
-      if (write_a2) p.a2_g[row0 + m] = g2;
-    }
-    s_g2[m] = g2;
-    s_slot[m] = slot;
-  }
-  __syncthreads();
-  const int nb0 = blockIdx.y * (4 * 16 * FN) + wave * 16 * FN;
-  const uint8_t* wc = p.w2c + static_cast<int64_t>(e) * H * (I / 2);
-  const uint8_t* ws = p.w2s + static_cast<int64_t>(e) * H * (I / 16);
-  f32x4 acc[FN][FM];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kc = 0; kc < I; kc += kKC) {
-    const int nsteps = min(kKC, I - kc) / 128;
-    uint4 wcodes[FN][4];
-    uint32_t wsc[FN][4];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t n = nb0 + f * 16 + r16;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < nsteps) load_weight_piece(wc, ws, n, I, kc / 128 + s, g, wcodes[f][s], wsc[f][s]);
-    }
-    __syncthreads();
-    // stage: re-quantize 16-element blocks of act, dequantize to fp16
-    const int blocks_per_row = nsteps * 8;
-    const int items = MT * blocks_per_row;
-    for (int it = threadIdx.x; it < items; it += 256) {
-      const int m = it / blocks_per_row;
-      const int kb = (it % blocks_per_row) * 16;
-      half8* dst = reinterpret_cast<half8*>(&lds[m][kb]);
-      if (m < nrows) {
-        const int64_t row = row0 + m;
-        const float4* src = reinterpret_cast<const float4*>(p.act + row * I + kc + kb);
-        float f[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = src[q];
-          f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
-        }
-        uint32_t lo, hi;
-        const uint32_t sb = quantize_block16(f, s_g2[m], lo, hi);
-        const half2v sc = e4m3_half2(sb);
-        dst[0] = dequant8_f16(lo, sc);
-        dst[1] = dequant8_f16(hi, sc);
-        if (write_a2) {
-          *reinterpret_cast<uint2*>(p.a2_codes + row * (I / 2) + (kc + kb) / 2) = make_uint2(lo, hi);
-          p.a2_scales[row * (I / 16) + (kc + kb) / 16] = static_cast<uint8_t>(sb);
-        }
-      } else {
-        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        dst[0] = z; dst[1] = z;
-      }
-    }
-    __syncthreads();
-    mma_chunk<FM, FN>(lds, nsteps, wcodes, wsc, acc, g, r16);
-  }
-
-  const float wginv = 1.0f / p.w2g[e];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = fm * 16 + r16;
-    if (m >= nrows) continue;
-    const float alpha = (1.0f / s_g2[m]) * wginv;
-    const int64_t row = row0 + m;
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int n = nb0 + f * 16 + 4 * g;
-      const float y0 = acc[f][fm][0] * alpha, y1 = acc[f][fm][1] * alpha;
-      const float y2 = acc[f][fm][2] * alpha, y3 = acc[f][fm][3] * alpha;
-      if (p.deterministic) {
-        *reinterpret_cast<float4*>(p.y + row * H + n) = make_float4(y0, y1, y2, y3);
-      } else {
-        const int slot = s_slot[m];
-        const float w = p.topk_w[slot];
-        float* dst = p.out_acc + static_cast<int64_t>(slot / p.k) * H + n;
-        atomicAdd(dst + 0, w * y0);
-        atomicAdd(dst + 1, w * y1);
-        atomicAdd(dst + 2, w * y2);
-        atomicAdd(dst + 3, w * y3);
-      }
-    }
-  }
 }
 
 // Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[inv[t, j], n]) in slot
@@ -538,19 +259,45 @@ __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Scale layout for the GEMMs: row-major [rows, K/16] -> [rows][g][step][2]
-// with block b = 8*step + 2*g + h, so that lane group g finds the two scales
-// of its 32-code piece of K step `step` as one 16-bit word.
+// Weight packing into the fragment-major layout (see kernels.hpp).  One
+// thread per 16-byte destination chunk.
 // ---------------------------------------------------------------------------
-__global__ void swizzle_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                      int64_t rows, int K) {
-  const int nb = K / 16;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * nb) return;
-  const int64_t row = i / nb;
-  const int b = static_cast<int>(i % nb);
-  const int step = b / 8, gg = (b % 8) / 2, h = b % 2;
-  dst[row * nb + gg * (K / 64) + step * 2 + h] = src[i];
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                  int64_t rows, int K) {
+  const int S = ksteps(K);
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= rows / 16 * S * 64) return;
+  const int l = static_cast<int>(c & 63);
+  const int64_t is = c >> 6;
+  const int64_t i = is / S;
+  const int st = static_cast<int>(is - i * S);
+  const int64_t row = 16 * i + (l & 15);
+  const uint4 v = *reinterpret_cast<const uint4*>(src + row * (K / 2) + 64 * st + 16 * (l >> 4));
+  *reinterpret_cast<uint4*>(dst + c * 16) = v;
+}
+
+__global__ void pack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                   int64_t rows, int K) {
+  const int S = ksteps(K), Q = sgroups(K);
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= rows / 16 * Q * 64) return;
+  const int l = static_cast<int>(c & 63);
+  const int64_t iq = c >> 6;
+  const int64_t i = iq / Q;
+  const int q = static_cast<int>(iq - i * Q);
+  const int64_t row = 16 * i + (l & 15);
+  const int g = l >> 4;
+  uint8_t out[16];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int st = 8 * q + t;
+    const bool ok = st < S;
+    out[2 * t] = ok ? src[row * (K / 16) + 8 * st + 2 * g] : 0;
+    out[2 * t + 1] = ok ? src[row * (K / 16) + 8 * st + 2 * g + 1] : 0;
+  }
+  uint4 v;
+  __builtin_memcpy(&v, out, 16);
+  *reinterpret_cast<uint4*>(dst + c * 16) = v;
 }
 
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
@@ -558,10 +305,17 @@ __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict
   if (i < n) dst[i] = src[i];
 }
 
-hipError_t launch_swizzle_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                                 hipStream_t s) {
-  const int64_t n = rows * (K / 16);
-  swizzle_scales_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(src, dst, rows, static_cast<int>(K));
+hipError_t launch_pack_codes(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                             hipStream_t s) {
+  const int64_t n = rows / 16 * ksteps(static_cast<int>(K)) * 64;
+  pack_codes_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(src, dst, rows, static_cast<int>(K));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                              hipStream_t s) {
+  const int64_t n = rows / 16 * sgroups(static_cast<int>(K)) * 64;
+  pack_scales_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(src, dst, rows, static_cast<int>(K));
   return hipGetLastError();
 }
 
@@ -570,42 +324,30 @@ hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t 
   return hipGetLastError();
 }
 
-constexpr int kG1FNH = 1;  // gate (and up) fragments per wave in GEMM1
-constexpr int kG2FN = 2;   // fragments per wave in GEMM2
-
-int gemm1_cols_per_block() { return 4 * 16 * kG1FNH; }
-
-template <int FM>
-static void launch_gemms(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  const int n1 = p.I / (4 * 16 * kG1FNH);
-  moe_gemm1_kernel<FM, kG1FNH><<<dim3(max_tiles, n1), 256, 0, s>>>(p);
-  if (ev) (void)hipEventRecord(ev[2], s);
-  const int n2 = p.H / (4 * 16 * kG2FN);
-  moe_gemm2_kernel<FM, kG2FN><<<dim3(max_tiles, n2), 256, 0, s>>>(p, n1);
-  if (ev) (void)hipEventRecord(ev[3], s);
+template <int NB>
+static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s) {
+  if (p.E <= 128)
+    moe_route_kernel<NB, 2><<<nblocks, 256, 0, s>>>(p, tpb);
+  else if (p.E <= 256)
+    moe_route_kernel<NB, 4><<<nblocks, 256, 0, s>>>(p, tpb);
+  else
+    moe_route_kernel<NB, kMaxExperts / kWave><<<nblocks, 256, 0, s>>>(p, tpb);
 }
 
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* ev) {
   if (ev) (void)hipEventRecord(ev[0], s);
-  int tpb = (p.T + 255) / 256;
-  tpb = ((tpb + 3) / 4) * 4;
-  if (tpb < 16) tpb = 16;
-  if (tpb > kMaxTokensPerBlock) tpb = kMaxTokensPerBlock;
+  const int tpb = route_tokens_per_block(p.T);
   const int nblocks = (p.T + tpb - 1) / tpb;
   switch (quant_nb_for_cols(p.H)) {
-    case 1: moe_route_kernel<1><<<nblocks, 256, 0, s>>>(p, tpb); break;
-    case 2: moe_route_kernel<2><<<nblocks, 256, 0, s>>>(p, tpb); break;
-    case 4: moe_route_kernel<4><<<nblocks, 256, 0, s>>>(p, tpb); break;
-    case 8: moe_route_kernel<8><<<nblocks, 256, 0, s>>>(p, tpb); break;
-    default: moe_route_kernel<0><<<nblocks, 256, 0, s>>>(p, tpb); break;
+    case 1: launch_route<1>(p, nblocks, tpb, s); break;
+    case 2: launch_route<2>(p, nblocks, tpb, s); break;
+    case 4: launch_route<4>(p, nblocks, tpb, s); break;
+    case 8: launch_route<8>(p, nblocks, tpb, s); break;
+    default: launch_route<0>(p, nblocks, tpb, s); break;
   }
   if (ev) (void)hipEventRecord(ev[1], s);
-  switch (p.mt) {
-    case 16: launch_gemms<1>(p, max_tiles, s, ev); break;
-    case 32: launch_gemms<2>(p, max_tiles, s, ev); break;
-    default: launch_gemms<4>(p, max_tiles, s, ev); break;
-  }
+  launch_grouped_gemms(p, max_tiles, s, ev);
   const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 8);
   moe_finalize_kernel<<<static_cast<unsigned>((nthreads + 255) / 256), 256, 0, s>>>(p);
   if (ev) (void)hipEventRecord(ev[4], s);
