@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=2, help="copies of the expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each timed forward from a captured HIP graph (as decode serving does)")
     return ap.parse_args()
 
 
@@ -130,24 +132,61 @@ def main():
     for i in range(args.warmup):
         layers[i % len(layers)].forward_into(x, logits, out)
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
     lib = binding.lib()
     lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
-    arrs = [(ctypes.c_void_p * 5)(*[e.value for e in step]) for step in evs]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ly = layers[i % len(layers)]
-        lib.moe_workspace_set_stage_events(ly.handle, arrs[i])
-        ly.forward_into(x, logits, out)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.graph:
+        # one graph per weight copy; the stage events are recorded inside the
+        # graph, so every replay re-records them on the replay stream
+        nrot = len(layers)
+        evs = [[hip.event() for _ in range(5)] for _ in range(nrot)]
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for r, ly in enumerate(layers):
+                lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in evs[r]]))
+                ly.forward_into(x, logits, out)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    ly.forward_into(x, logits, out)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        per_stage = {s: [] for s in stages}
+        t_total = 0.0
+        for i in range(args.steps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graphs[i % nrot].replay()
+            torch.cuda.synchronize()
+            t_total += time.perf_counter() - t0
+            step = evs[i % nrot]
+            for j, s in enumerate(stages):
+                per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
+        # back-to-back replays for the wall-clock throughput
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % nrot].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
+        arrs = [(ctypes.c_void_p * 5)(*[e.value for e in step]) for step in evs]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ly = layers[i % len(layers)]
+            lib.moe_workspace_set_stage_events(ly.handle, arrs[i])
+            ly.forward_into(x, logits, out)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per_stage = {s: [] for s in stages}
+        for step in evs:
+            for j, s in enumerate(stages):
+                per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
     for ly in layers:
         lib.moe_workspace_set_stage_events(ly.handle, None)
-    per_stage = {s: [] for s in stages}
-    for step in evs:
-        for j, s in enumerate(stages):
-            per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
     mean_ms = {s: float(np.mean(v)) for s, v in per_stage.items()}
     for step in evs:
         for e in step:
@@ -194,7 +233,8 @@ def main():
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": f"nvfp4_moe_layer_{L.name}", "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
-                   "weights_rotated": args.rotate, "parallelism": "none (1 GPU)"},
+                   "weights_rotated": args.rotate, "hip_graph": bool(args.graph),
+                   "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "cpu_baseline": cpu,

@@ -239,6 +239,9 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(FwdParams p) {
   }
   const int nsteps = S;
   const int last = nsteps - 1;
+  // Loads past the last step go to a 1 KB always-cached dummy block instead
+  // (keeps every load unconditional without re-reading weights).
+  const uint8_t* dummy = p.dummy + 16 * lane;
   // weights first, so that they are in flight while the token operand stages
   uint4 wsc_cur[FN];
 #pragma unroll
@@ -246,9 +249,8 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(FwdParams p) {
   uint4 wb[kStreamDepth][FN];
 #pragma unroll
   for (int d = 0; d < kStreamDepth; ++d) {
-    const int sl = min(d, last);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) wb[d][f] = load_stream16(cptr[f] + 1024 * sl);
+    for (int f = 0; f < FN; ++f) wb[d][f] = load_stream16(d <= last ? cptr[f] + 1024 * d : dummy);
   }
 
   // Stage the token operand with direct global->LDS copies (no registers):
@@ -287,9 +289,10 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(FwdParams p) {
   for (int s8 = 0; s8 < nsteps; s8 += 8) {
     // scales of the next 8 steps (one 16-byte load per fragment row)
     uint4 wsc_nxt[FN];
-    const int ng = min(s8 + 8, last) / 8;
+    const bool more = s8 + 8 <= last;
 #pragma unroll
-    for (int f = 0; f < FN; ++f) wsc_nxt[f] = *reinterpret_cast<const uint4*>(sptr[f] + 1024 * ng);
+    for (int f = 0; f < FN; ++f)
+      wsc_nxt[f] = *reinterpret_cast<const uint4*>(more ? sptr[f] + 1024 * ((s8 + 8) / 8) : dummy);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const int s = s8 + d;
@@ -327,9 +330,9 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(FwdParams p) {
           }
         }
       }
-      const int sn = min(s + kStreamDepth, last);
+      const int sn = s + kStreamDepth;
 #pragma unroll
-      for (int f = 0; f < FN; ++f) wb[slot][f] = load_stream16(cptr[f] + 1024 * sn);
+      for (int f = 0; f < FN; ++f) wb[slot][f] = load_stream16(sn <= last ? cptr[f] + 1024 * sn : dummy);
     }
 #pragma unroll
     for (int f = 0; f < FN; ++f) wsc_cur[f] = wsc_nxt[f];
@@ -497,48 +500,69 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-constexpr int kStreamFN = 2;  // fragments per wave (GEMM1: 1 gate + 1 up)
 constexpr int kTiledFN = 2;
 
 int stream_lds_bytes(int fm, int K) { return 16 * fm * ((K / 2 + 16) + (K / 16 + 4)); }
 
-void choose_gemm(int64_t T, int H, int I, int E, int k, int* mt, int* kind, int* g1_bands) {
-  const int64_t R = T * k;
+// Kernel family, rows per tile and fragments per wave for a forward of T
+// tokens.  Stream kernels use 4 fragments per wave (the token operand's
+// dequantization is shared by more weight rows) when that still gives at
+// least two blocks per CU, else 2 (more, smaller blocks for tiny batches).
+void choose_gemm(int64_t T, FwdParams* p) {
+  const int H = p->H, I = p->I, E = p->E;
+  const int64_t R = T * p->k;
   const int64_t active = R < E ? R : E;
   const int64_t avg = (R + active - 1) / (active > 0 ? active : 1);
   const int Kmax = H > I ? H : I;
-  const bool bands_fit = H % (64 * kStreamFN) == 0 && I % (64 * (kStreamFN / 2)) == 0;
+  const bool bands_fit = H % 128 == 0 && I % 64 == 0;
   if (bands_fit && avg <= 16 && stream_lds_bytes(1, Kmax) <= 65536) {
-    *mt = 16;
-    *kind = kGemmStream;
+    p->mt = 16;
+    p->gemm_kind = kGemmStream;
   } else if (bands_fit && avg <= 32 && stream_lds_bytes(2, Kmax) <= 65536) {
-    *mt = 32;
-    *kind = kGemmStream;
+    p->mt = 32;
+    p->gemm_kind = kGemmStream;
   } else {
-    *mt = 64;
-    *kind = kGemmTiled;
+    p->mt = 64;
+    p->gemm_kind = kGemmTiled;
   }
-  *g1_bands = *kind == kGemmStream ? I / (64 * (kStreamFN / 2)) : I / (64 * (kTiledFN / 2));
+  if (p->gemm_kind == kGemmStream) {
+    const int64_t tiles = (R + p->mt - 1) / p->mt > active ? (R + p->mt - 1) / p->mt : active;
+    const int64_t want = 2 * 256;
+    p->g1_fn = (I % 128 == 0 && tiles * (I / 128) >= want) ? 4 : 2;
+    p->g2_fn = (H % 256 == 0 && tiles * (H / 256) >= want) ? 4 : 2;
+    p->g1_bands = I / (32 * p->g1_fn);
+  } else {
+    p->g1_fn = p->g2_fn = kTiledFN;
+    p->g1_bands = I / (64 * (kTiledFN / 2));
+  }
+}
+
+template <int FM, int FN1, int FN2>
+static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
+  const int nb1 = p.I / (32 * FN1);
+  moe_stream_kernel<FM, FN1, 0><<<dim3(max_tiles, nb1), 256, stream_lds_bytes(FM, p.H), s>>>(p);
+  if (ev) (void)hipEventRecord(ev[2], s);
+  moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
+  const int nb2 = p.H / (64 * FN2);
+  moe_stream_kernel<FM, FN2, 1><<<dim3(max_tiles, nb2), 256, stream_lds_bytes(FM, p.I), s>>>(p);
+  if (ev) (void)hipEventRecord(ev[3], s);
 }
 
 template <int FM>
-static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  const int nb1 = p.I / (64 * (kStreamFN / 2));
-  moe_stream_kernel<FM, kStreamFN, 0><<<dim3(max_tiles, nb1), 256, stream_lds_bytes(FM, p.H), s>>>(p);
-  if (ev) (void)hipEventRecord(ev[2], s);
-  moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-  const int nb2 = p.H / (64 * kStreamFN);
-  moe_stream_kernel<FM, kStreamFN, 1><<<dim3(max_tiles, nb2), 256, stream_lds_bytes(FM, p.I), s>>>(p);
-  if (ev) (void)hipEventRecord(ev[3], s);
+static void launch_stream_fm(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
+  if (p.g1_fn == 4 && p.g2_fn == 4) launch_stream<FM, 4, 4>(p, max_tiles, s, ev);
+  else if (p.g1_fn == 4) launch_stream<FM, 4, 2>(p, max_tiles, s, ev);
+  else if (p.g2_fn == 4) launch_stream<FM, 2, 4>(p, max_tiles, s, ev);
+  else launch_stream<FM, 2, 2>(p, max_tiles, s, ev);
 }
 
 hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s,
                                 hipEvent_t const* ev) {
   if (p.gemm_kind == kGemmStream) {
     if (p.mt == 16)
-      launch_stream<1>(p, max_tiles, s, ev);
+      launch_stream_fm<1>(p, max_tiles, s, ev);
     else
-      launch_stream<2>(p, max_tiles, s, ev);
+      launch_stream_fm<2>(p, max_tiles, s, ev);
   } else {
     const int nb1 = p.I / (64 * (kTiledFN / 2));
     moe_tiled_kernel<4, kTiledFN, 0><<<dim3(max_tiles, nb1), 256, 0, s>>>(p);

@@ -50,6 +50,7 @@ struct FwdParams {
   int T, H, I, E, k, R;
   int mt;             // rows per M-tile of the grouped GEMMs
   int gemm_kind;      // GemmKind
+  int g1_fn, g2_fn;   // stream kernels: 16-row weight fragments per wave
   int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
   // caller tensors
@@ -87,6 +88,7 @@ struct FwdParams {
   const uint8_t* w2c;
   const uint8_t* w2s;
   const float* w2g;
+  const uint8_t* dummy;  // 1 KB of zeros: target of loads past the last K step
 };
 
 // quantize.hip
@@ -99,7 +101,7 @@ hipError_t launch_quantize_experts(const float* w, int64_t experts, int64_t rows
 
 // gemm_kernels.hip
 // Rows per tile and kernel family for a forward of T tokens.
-void choose_gemm(int64_t T, int H, int I, int E, int k, int* mt, int* kind, int* g1_bands);
+void choose_gemm(int64_t T, FwdParams* p);
 // Dynamic LDS bytes of the stream kernel for reduction length K.
 int stream_lds_bytes(int fm, int K);
 hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s,

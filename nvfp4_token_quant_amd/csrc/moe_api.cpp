@@ -91,6 +91,7 @@ struct moe_workspace {
   uint8_t* w2s;
   float* w13g;
   float* w2g;
+  uint8_t* dummy;
   // optional stage-timing events (caller-owned)
   bool timing;
   hipEvent_t events[5];
@@ -133,6 +134,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->w2s), nvfp4::packed_scale_bytes(E * H, static_cast<int>(I)));
   f(reinterpret_cast<void**>(&w->w13g), E * 4);
   f(reinterpret_cast<void**>(&w->w2g), E * 4);
+  f(reinterpret_cast<void**>(&w->dummy), 1024);
 }
 
 void free_all(moe_workspace* w) {
@@ -287,6 +289,7 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = nvfp4::launch_fill_u32(w->ticket, 1, 0u, s);
+  if (e == hipSuccess) e = nvfp4::launch_fill_u32(reinterpret_cast<uint32_t*>(w->dummy), 256, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     free_all(w);
@@ -351,7 +354,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.E = static_cast<int>(E);
   p.k = c.top_k;
   p.R = static_cast<int>(T * c.top_k);
-  nvfp4::choose_gemm(T, p.H, p.I, p.E, p.k, &p.mt, &p.gemm_kind, &p.g1_bands);
+  nvfp4::choose_gemm(T, &p);
   p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
   p.x = static_cast<const uint16_t*>(x_dev);
   p.logits = logits_dev;
@@ -383,6 +386,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.w2c = ws->w2c;
   p.w2s = ws->w2s;
   p.w2g = ws->w2g;
+  p.dummy = ws->dummy;
   const int64_t max_tiles = tiles_bound(p.R, E, p.mt);
   if (max_tiles > ws->max_tiles_cap) return fail(NVFP4_ERR_INVALID_ARG, "internal: tile bound exceeds capacity");
   hipError_t e = nvfp4::launch_moe_forward(p, static_cast<int>(max_tiles), static_cast<hipStream_t>(stream),

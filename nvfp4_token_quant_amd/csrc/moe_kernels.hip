@@ -28,6 +28,61 @@
 namespace nvfp4 {
 
 // ---------------------------------------------------------------------------
+// Router reductions.  A candidate is the 64-bit key (order-preserving bits of
+// the logit) << 32 | ~expert, so the larger key is the larger logit and, on
+// equal logits, the smaller expert index.  Reductions over a 16-lane DPP row
+// use quad permutes (xor 1, xor 2) and row rotates (4, 8), a few cycles each.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = static_cast<uint32_t>(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return static_cast<int>(~static_cast<uint32_t>(k)); }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+__device__ __forceinline__ uint64_t row16_max(uint64_t k) {
+  uint64_t o = dpp_u64<kDppXor1>(k); k = o > k ? o : k;
+  o = dpp_u64<kDppXor2>(k); k = o > k ? o : k;
+  o = dpp_u64<kDppRor4>(k); k = o > k ? o : k;
+  o = dpp_u64<kDppRor8>(k); k = o > k ? o : k;
+  return k;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppRor4>(v);
+  v += dpp_f32<kDppRor8>(v);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = row16_max(k);
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), o, kWave);
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), o, kWave);
+    const uint64_t ok = (static_cast<uint64_t>(hi) << 32) | lo;
+    k = ok > k ? ok : k;
+  }
+  return k;
+}
+
+// ---------------------------------------------------------------------------
 // Router: the k largest logits of one token, ties to the smaller expert
 // index, slots in descending order; weights = exp(l_j - l_0) normalized over
 // the k slots (the softmax over all experts restricted to the chosen k).
@@ -37,53 +92,33 @@ template <int kPerLane>
 __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
                                  int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                                  int32_t* __restrict__ lds_ids, int lane) {
-  float v[kPerLane];
-  uint32_t avail = 0;
+  // Unconditional loads (index clamped; invalid candidates get key 0) so
+  // that all of them are in flight at once.
+  uint64_t cand[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + kWave * i;
-    v[i] = 0.0f;
-    if (e < E) {
-      v[i] = lrow[e];
-      avail |= 1u << i;
-    }
+    const float v = lrow[e < E ? e : E - 1];
+    cand[i] = e < E ? route_key(v, e) : 0ull;
   }
-  int my_id = 0;
-  float my_v = 0.0f, top = 0.0f;
+  uint64_t mine = 0, top = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      if ((avail >> i) & 1u) {
-        if (bi == 0x7FFFFFFF || v[i] > bv) {  // ascending index: ties keep the smaller one
-          bv = v[i];
-          bi = lane + kWave * i;
-        }
-      }
-    }
+    for (int i = 0; i < kPerLane; ++i) best = cand[i] > best ? cand[i] : best;
+    best = wave_max_u64(best);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool take = (oi != 0x7FFFFFFF) &&
-                        (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-      bv = take ? ov : bv;
-      bi = take ? oi : bi;
-    }
-    if ((bi & (kWave - 1)) == lane) avail &= ~(1u << (bi / kWave));
-    if (lane == j) {
-      my_id = bi;
-      my_v = bv;
-    }
-    if (j == 0) top = bv;
+    for (int i = 0; i < kPerLane; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
+    if (lane == j) mine = best;
+    if (j == 0) top = best;
   }
-  const float ex = lane < k ? expf(my_v - top) : 0.0f;
+  const float ex = lane < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    ids_out[lane] = my_id;
+    const int id = key_expert(mine);
+    ids_out[lane] = id;
     w_out[lane] = ex / sum;
-    lds_ids[lane] = my_id;
+    lds_ids[lane] = id;
   }
 }
 
@@ -226,6 +261,171 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   build_schedule_last_block(p, gridDim.x, tpb);
 }
 
+// ---------------------------------------------------------------------------
+// Prologue for small batches (T <= 256, E <= 256, T*k <= 2048): block 0
+// routes every token and builds the whole schedule in LDS (no cross-block
+// communication); blocks 1.. quantize 8 token rows each, one per wave, at the
+// same time.
+//
+// Routing uses 16 lanes per token (4 tokens per wave at once): lane j of a
+// group holds experts j, j + 16, ...  Stable ranks come from 64-entry chunks:
+// a lane's rank among equal experts in its chunk is the popcount of the lanes
+// below it whose expert id matches bit for bit (one ballot per id bit); the
+// per-chunk counts are then scanned down the chunks per expert.
+// ---------------------------------------------------------------------------
+constexpr int kSmallMaxT = 256, kSmallMaxE = 256, kSmallMaxR = 2048;
+constexpr int kSmallThreads = 1024;  // 16 waves: 64 tokens routed per pass
+constexpr int kSmallWaves = kSmallThreads / 64;
+
+template <int KPL>
+__device__ void route_token_group16(const float* __restrict__ lrow, int E, int k, int gl,
+                                    int& my_id, float& my_w) {
+  uint64_t cand[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = gl + 16 * i;
+    const float v = lrow[e < E ? e : E - 1];
+    cand[i] = e < E ? route_key(v, e) : 0ull;
+  }
+  uint64_t mine = 0, top = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) best = cand[i] > best ? cand[i] : best;
+    best = row16_max(best);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
+    if (gl == j) mine = best;
+    if (j == 0) top = best;
+  }
+  const float ex = gl < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
+  const float sum = row16_sum(ex);
+  my_id = key_expert(mine);
+  my_w = ex / sum;
+}
+
+
+template <int NB, int KPL>
+__global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdParams p) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int H = p.H, k = p.k, E = p.E, T = p.T, R = p.R;
+  if (blockIdx.x > 0) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * kSmallWaves + wave;
+    if (t < T) {
+      quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
+                            p.xq_g + t, lane);
+      if (!p.deterministic) {
+        float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+        for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
+  __shared__ int32_t s_ids[kSmallMaxR];
+  __shared__ int32_t s_rank[kSmallMaxR];
+  __shared__ int32_t s_cnt[kSmallMaxR / 64][kSmallMaxE];
+  __shared__ int32_t s_off[kSmallMaxE];
+  __shared__ int32_t s_tbase[kSmallMaxE];
+  __shared__ int32_t s_part[kSmallThreads][2];
+  const int tid = threadIdx.x;
+  // 1. routing, 4 tokens per wave at a time
+  const int grp = lane >> 4, gl = lane & 15;
+  for (int t0 = wave * 4; t0 < T; t0 += kSmallWaves * 4) {
+    const int t = t0 + grp;
+    const int tc = t < T ? t : T - 1;
+    int id;
+    float w;
+    route_token_group16<KPL>(p.logits + static_cast<int64_t>(tc) * E, E, k, gl, id, w);
+    if (t < T && gl < k) {
+      p.topk_ids[t * k + gl] = id;
+      p.topk_w[t * k + gl] = w;
+      s_ids[t * k + gl] = id;
+    }
+  }
+  for (int i = tid; i < (kSmallMaxR / 64) * kSmallMaxE; i += kSmallThreads) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  // 2. ranks inside 64-entry chunks
+  const int nch = (R + 63) / 64;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int c = wave; c < nch; c += kSmallWaves) {
+    const int i = 64 * c + lane;
+    const bool valid = i < R;
+    const int e = valid ? s_ids[i] : 0;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bm = __ballot((e >> b) & 1);
+      mask &= ((e >> b) & 1) ? bm : ~bm;
+    }
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    if (valid) {
+      s_rank[i] = rank;
+      if (rank == 0) s_cnt[c][e] = __popcll(mask);
+    }
+  }
+  __syncthreads();
+  // 3. per expert: exclusive scan down the chunks
+  int tot = 0, ntile = 0;
+  if (tid < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = s_cnt[c][tid];
+      s_cnt[c][tid] = tot;
+      tot += v;
+    }
+    ntile = (tot + p.mt - 1) / p.mt;
+    p.counts[tid] = tot;
+  }
+  s_part[tid][0] = tot;
+  s_part[tid][1] = ntile;
+  __syncthreads();
+  // 4. exclusive scans over experts (rows and tiles)
+  for (int o = 1; o < kSmallMaxE; o <<= 1) {
+    int a0 = 0, a1 = 0;
+    if (tid >= o) {
+      a0 = s_part[tid - o][0];
+      a1 = s_part[tid - o][1];
+    }
+    __syncthreads();
+    s_part[tid][0] += a0;
+    s_part[tid][1] += a1;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int off = s_part[tid][0] - tot, tb = s_part[tid][1] - ntile;
+    s_off[tid] = off;
+    s_tbase[tid] = tb;
+    p.offsets[tid] = off;
+    for (int i = 0; i < ntile; ++i)
+      p.tiles[tb + i] = make_int4(tid, off + i * p.mt, min(p.mt, tot - i * p.mt), 0);
+  }
+  if (tid == kSmallMaxE - 1) {
+    p.offsets[E] = s_part[kSmallMaxE - 1][0];
+    *p.n_tiles = s_part[kSmallMaxE - 1][1];
+  }
+  __syncthreads();
+  // 5. placement
+  for (int i = tid; i < R; i += kSmallThreads) {
+    const int e = s_ids[i];
+    const int row = s_off[e] + s_cnt[i / 64][e] + s_rank[i];
+    p.perm[row] = i;
+    p.inv[i] = row;
+  }
+}
+
+bool use_small_prologue(const FwdParams& p) {
+  return p.T <= kSmallMaxT && p.E <= kSmallMaxE && p.R <= kSmallMaxR;
+}
+
+template <int NB>
+static void launch_prologue_small(const FwdParams& p, hipStream_t s) {
+  const int blocks = 1 + (p.T + kSmallWaves - 1) / kSmallWaves;
+  if (p.E <= 16) moe_prologue_small_kernel<NB, 1><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 32) moe_prologue_small_kernel<NB, 2><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 64) moe_prologue_small_kernel<NB, 4><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 128) moe_prologue_small_kernel<NB, 8><<<blocks, kSmallThreads, 0, s>>>(p);
+  else moe_prologue_small_kernel<NB, 16><<<blocks, kSmallThreads, 0, s>>>(p);
+}
+
 // Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[inv[t, j], n]) in slot
 // order (deterministic), or bf16_rne(out_acc[t, n]) after the atomic epilogue.
 // One thread per 8 output columns.
@@ -337,14 +537,24 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* ev) {
   if (ev) (void)hipEventRecord(ev[0], s);
-  const int tpb = route_tokens_per_block(p.T);
-  const int nblocks = (p.T + tpb - 1) / tpb;
-  switch (quant_nb_for_cols(p.H)) {
-    case 1: launch_route<1>(p, nblocks, tpb, s); break;
-    case 2: launch_route<2>(p, nblocks, tpb, s); break;
-    case 4: launch_route<4>(p, nblocks, tpb, s); break;
-    case 8: launch_route<8>(p, nblocks, tpb, s); break;
-    default: launch_route<0>(p, nblocks, tpb, s); break;
+  if (use_small_prologue(p)) {
+    switch (quant_nb_for_cols(p.H)) {
+      case 1: launch_prologue_small<1>(p, s); break;
+      case 2: launch_prologue_small<2>(p, s); break;
+      case 4: launch_prologue_small<4>(p, s); break;
+      case 8: launch_prologue_small<8>(p, s); break;
+      default: launch_prologue_small<0>(p, s); break;
+    }
+  } else {
+    const int tpb = route_tokens_per_block(p.T);
+    const int nblocks = (p.T + tpb - 1) / tpb;
+    switch (quant_nb_for_cols(p.H)) {
+      case 1: launch_route<1>(p, nblocks, tpb, s); break;
+      case 2: launch_route<2>(p, nblocks, tpb, s); break;
+      case 4: launch_route<4>(p, nblocks, tpb, s); break;
+      case 8: launch_route<8>(p, nblocks, tpb, s); break;
+      default: launch_route<0>(p, nblocks, tpb, s); break;
+    }
   }
   if (ev) (void)hipEventRecord(ev[1], s);
   launch_grouped_gemms(p, max_tiles, s, ev);

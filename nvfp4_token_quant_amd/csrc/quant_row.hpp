@@ -34,20 +34,18 @@ __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
   if constexpr (NB > 0) {
     uint4 v[NB][2];
     float am = 0.0f;
+    // Unconditional loads (block index clamped) so that they are all in
+    // flight together; blocks past the row end count as zeros.
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int b = lane + kWave * i;
-      if (b < nblk) {
-        const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
-        v[i][0] = load_stream16(p);
-        v[i][1] = load_stream16(p + 1);
-      } else {
-        v[i][0] = make_uint4(0, 0, 0, 0);
-        v[i][1] = make_uint4(0, 0, 0, 0);
-      }
+      const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * (b < nblk ? b : nblk - 1));
+      v[i][0] = load_stream16(p);
+      v[i][1] = load_stream16(p + 1);
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) am = fmaxf(am, amax16_bf16(v[i][0], v[i][1]));
+    for (int i = 0; i < NB; ++i)
+      if (lane + kWave * i < nblk) am = fmaxf(am, amax16_bf16(v[i][0], v[i][1]));
     const float g = global_scale(wave_max(am));
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
