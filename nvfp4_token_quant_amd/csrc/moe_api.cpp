@@ -17,7 +17,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/nvfp4_moe.h"
+#include "nvfp4_moe.h"
 #include "kernels.hpp"
 
 namespace {

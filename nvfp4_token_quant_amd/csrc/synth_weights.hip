@@ -13,7 +13,7 @@
 
 #include <string>
 
-#include "../../include/nvfp4_synth.h"
+#include "nvfp4_synth.h"
 
 namespace {
 
