@@ -22,6 +22,12 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// Materializes v in a register at this point.  Loads that feed it are then
+// issued before any later branch instead of being sunk into the branches that
+// use them (which serializes one memory round trip per branch).
+template <typename T>
+__device__ __forceinline__ void keep_issued(T& v) { asm volatile("" : "+v"(v)); }
+
 constexpr int kBlock = 16;            // elements per E4M3 block scale
 constexpr float kGlobalNum = 2688.0f;  // 448 (E4M3 max) * 6 (E2M1 max)
 

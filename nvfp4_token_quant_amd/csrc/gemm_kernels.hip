@@ -46,18 +46,18 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 // ---------------------------------------------------------------------------
 
 // GEMM1: per lane, fragment pair (gate fh, up fh) holds h[n = c0 + 16 fh + 4g + i]
-// for row m = 16 fm + r16.  act = silu(h_gate) * h_up in fp32, stored with the
-// band's per-row amax.
+// for row m = 16 fm + r16; ginv[fm] = 1 / (that row's token global scale).
+// act = silu(h_gate) * h_up in fp32, stored with the row's amax over these
+// columns in s_amax[wave][m].
 template <int FM, int FNH>
 __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&acc)[2 * FNH][FM],
-                                            int e, int row0, int nrows, int c0,
-                                            const float* s_ginv, float (*s_amax)[16 * FM], int wave,
-                                            int g, int r16) {
+                                            int e, int row0, int nrows, int c0, const float (&ginv)[FM],
+                                            float (*s_amax)[16 * FM], int wave, int g, int r16) {
   const float wginv = 1.0f / p.w13g[e];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int m = fm * 16 + r16;
-    const float alpha = s_ginv[m] * wginv;
+    const float alpha = ginv[fm] * wginv;
     float am = 0.0f;
 #pragma unroll
     for (int fh = 0; fh < FNH; ++fh) {
@@ -81,8 +81,8 @@ __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&ac
   }
 }
 
-// The band's per-row amax of act (one partial per GEMM1 column band; GEMM2's
-// staging or the re-quantization kernel reduces them).
+// The block's per-row amax of act over its columns (one partial per GEMM1
+// column band; the re-quantization kernel reduces them).
 template <int MT>
 __device__ __forceinline__ void g1_store_band_amax(const FwdParams& p, float (*s_amax)[MT], int row0,
                                                    int nrows) {
@@ -108,18 +108,20 @@ __device__ __forceinline__ uint32_t requant_block(const float* __restrict__ src,
   return quantize_block16(f, g2, lo, hi);
 }
 
-// GEMM2: per lane, fragment f holds y[n = n0 + 16 f + 4g + i] of row m.
+// GEMM2: per lane, fragment f holds y[n = n0 + 16 f + 4g + i] of row m =
+// 16 fm + r16; ginv[fm] = 1 / (that row's a2 global scale), slot[fm] = its
+// t*k+j (atomic finalize only).
 template <int FM, int FN>
 __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&acc)[FN][FM], int e,
-                                            int row0, int nrows, int n0, const float* s_ginv,
-                                            const int* s_slot, int g, int r16) {
+                                            int row0, int nrows, int n0, const float (&ginv)[FM],
+                                            const int (&slot)[FM], int g, int r16) {
   const float wginv = 1.0f / p.w2g[e];
   const int H = p.H;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int m = fm * 16 + r16;
     if (m >= nrows) continue;
-    const float alpha = s_ginv[m] * wginv;
+    const float alpha = ginv[fm] * wginv;
     const int64_t row = row0 + m;
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
@@ -129,9 +131,8 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
       if (p.deterministic) {
         *reinterpret_cast<float4*>(p.y + row * H + n) = make_float4(y0, y1, y2, y3);
       } else {
-        const int slot = s_slot[m];
-        const float w = p.topk_w[slot];
-        float* dst = p.out_acc + static_cast<int64_t>(slot / p.k) * H + n;
+        const float w = p.topk_w[slot[fm]];
+        float* dst = p.out_acc + static_cast<int64_t>(slot[fm] / p.k) * H + n;
         atomicAdd(dst + 0, w * y0);
         atomicAdd(dst + 1, w * y1);
         atomicAdd(dst + 2, w * y2);
@@ -141,41 +142,27 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
   }
 }
 
-// Rows of the token operand for local row m of a tile: GEMM1 reads the
-// per-token quantized activations of token perm[row] / k, GEMM2 the
-// re-quantized activation of the expanded row itself.
-template <int MODE>
-__device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrows, int mt,
-                                          int* s_src, float* s_ginv, int* s_slot) {
-  if (static_cast<int>(threadIdx.x) < mt) {
-    const int m = threadIdx.x;
-    int src = -1, slot = -1;
-    float gi = 0.0f;
-    if (m < nrows) {
-      slot = p.perm[row0 + m];
-      src = MODE == 0 ? slot / p.k : row0 + m;
-      gi = 1.0f / (MODE == 0 ? p.xq_g[src] : p.a2_g[src]);
-    }
-    s_src[m] = src;
-    s_ginv[m] = gi;
-    if (s_slot) s_slot[m] = slot;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Stream kernel (few rows per expert: decode).  One block = one tile of up to
-// 16*FM rows x a band of 64*FN weight rows (4 waves x FN fragments of 16).
-// The tile's token operand is staged once in LDS as FP4 codes + E4M3 scales
-// (dynamic LDS: MT rows x (K/2 + 16) code bytes and (K/16 + 4) scale bytes);
-// each wave then walks K in 128-wide steps with the code pieces of the next
-// kStreamDepth steps in flight, and fetches the weight scales of 8 steps with
-// one 16-byte load (the GEMM scale layout keeps them contiguous).  Every load
-// of the loop is unconditional (steps past the end re-read the last one) and
-// issued in consumption order, so the waits only cover the oldest step.
-// MODE 0: GEMM1 (weights W13, FN/2 gate + FN/2 up fragments, SwiGLU);
-// MODE 1: GEMM2 (weights W2, FN output fragments).
+// 16*FM rows x 4/KS weight units; wave w takes unit w / KS and the K range
+// w % KS of it (KS waves split one unit's K and add their partial sums in LDS
+// at the end).  The tile's token operand is staged once in LDS as FP4 codes +
+// E4M3 scales (dynamic LDS: MT rows x (K/2 + 16) code bytes and (K/16 + 4)
+// scale bytes); each wave then walks its K range in 128-wide steps, one
+// 4.5 KB unit record per step, with the next kStreamDepth records in flight.
+//
+// Issue order.  Vector loads complete in issue order, so a wait for the
+// staging copies also waits for every weight load issued before them.  The
+// kernel therefore issues two weight steps, then the staging copies, waits,
+// and only then fills the rest of the prefetch window: the wave starts
+// computing as soon as its first records land instead of after all of them.
+// Every later load is unconditional (past the wave's range it reads a zero
+// dummy record), so each wait covers exactly the oldest step.
+// MODE 0: GEMM1 (W13 units: 2 gate + 2 up fragments, SwiGLU epilogue);
+// MODE 1: GEMM2 (W2 units: 4 output fragments).
 // ---------------------------------------------------------------------------
-constexpr int kStreamDepth = 8;
+constexpr int kStreamDepth = 5;
+constexpr int kStreamEarly = 2;  // steps issued before the staging copies
 
 // Copy `bytes` bytes from global memory to LDS with global_load_lds: one wave
 // instruction moves 64 x W bytes (lane l moves bytes [W l, W l + W) of the
@@ -194,171 +181,212 @@ __device__ __forceinline__ void copy_rows_to_lds(const uint8_t* src, uint8_t* ds
   }
 }
 
-template <int FM, int FN, int MODE>
-__global__ __launch_bounds__(256) void moe_stream_kernel(FwdParams p) {
+// One step's weight operand of a wave: 4 code pieces + the lane's 8 scale bytes.
+struct UnitStep {
+  uint4 c[kUnitFrags];
+  uint2 sc;
+};
+__device__ __forceinline__ void load_unit_step(UnitStep& u, const uint8_t* rec, int lane) {
+#pragma unroll
+  for (int f = 0; f < kUnitFrags; ++f) u.c[f] = load_stream16(rec + 1024 * f + 16 * lane);
+  u.sc = *reinterpret_cast<const uint2*>(rec + kRecCodeBytes + 8 * lane);
+}
+
+// acc[f][fm] += W_f (16 x 128 slice of step `step`) * token rows (fm) on the
+// token operand staged in LDS.
+template <int FM>
+__device__ __forceinline__ void unit_step_mfma(f32x4 (&acc)[kUnitFrags][FM], const UnitStep& w,
+                                               const uint8_t* lc, const uint8_t* ls, int cpitch,
+                                               int spitch, int step, int g, int r16) {
+  uint4 bc[FM];
+  half2v bsc[FM][2];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int r = fm * 16 + r16;
+    bc[fm] = *reinterpret_cast<const uint4*>(lc + r * cpitch + 64 * step + 16 * g);
+    const uint32_t sw = *reinterpret_cast<const uint16_t*>(ls + r * spitch + 8 * step + 2 * g);
+    bsc[fm][0] = e4m3_to_half2(sw);
+    bsc[fm][1] = e4m3_to_half2(sw >> 8);
+  }
+  half2v wsc[kUnitFrags][2];
+#pragma unroll
+  for (int f = 0; f < kUnitFrags; ++f) {
+    const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1));
+    wsc[f][0] = e4m3_to_half2(w16);
+    wsc[f][1] = e4m3_to_half2(w16 >> 8);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    half8 bq[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) bq[fm] = dequant8_f16(word_of(bc[fm], q), bsc[fm][q >> 1]);
+#pragma unroll
+    for (int f = 0; f < kUnitFrags; ++f) {
+      const half8 aq = dequant8_f16(word_of(w.c[f], q), wsc[f][q >> 1]);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[fm], acc[f][fm], 0, 0, 0);
+    }
+  }
+}
+
+template <int FM, int KS, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3 : 2))) void moe_stream_kernel(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MT = 16 * FM;
-  constexpr int FNH = FN / 2;
-  __shared__ int s_src[MT];
-  __shared__ int s_slot[MT];
-  __shared__ float s_ginv[MT];
-  __shared__ float s_aux[4][MT];
+  constexpr int UB = 4 / KS;  // units per block
+  constexpr int D = kStreamDepth;
+  __shared__ float s_amax[4][MT];
   if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
   const int4 td = p.tiles[blockIdx.x];
   const int e = td.x, row0 = td.y, nrows = td.z;
   const int K = MODE == 0 ? p.H : p.I;
+  const int S = ksteps(K);
   const int cpitch = K / 2 + 16, spitch = K / 16 + 4;
   uint8_t* lc = smem;
   uint8_t* ls = smem + MT * cpitch;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4, r16 = lane & 15;
 
-  // this wave's weight rows
-  // fragment f = 16 weight rows = one 16-row group of the fragment-major copy
-  const int S = ksteps(K), Q = sgroups(K);
-  const uint8_t* cptr[FN];
-  const uint8_t* sptr[FN];
-  int cbase;
-  if (MODE == 0) {
-    cbase = blockIdx.y * (64 * FNH) + wave * 16 * FNH;
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t n = f < FNH ? cbase + f * 16 : p.I + cbase + (f - FNH) * 16;
-      const int64_t grp = (static_cast<int64_t>(e) * 2 * p.I + n) / 16;
-      cptr[f] = p.w13c + grp * S * 1024 + 16 * lane;
-      sptr[f] = p.w13s + grp * Q * 1024 + 16 * lane;
-    }
-  } else {
-    cbase = blockIdx.y * (64 * FN) + wave * 16 * FN;
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t grp = (static_cast<int64_t>(e) * p.H + cbase + f * 16) / 16;
-      cptr[f] = p.w2c + grp * S * 1024 + 16 * lane;
-      sptr[f] = p.w2s + grp * Q * 1024 + 16 * lane;
-    }
-  }
-  const int nsteps = S;
-  const int last = nsteps - 1;
-  // Loads past the last step go to a 1 KB always-cached dummy block instead
-  // (keeps every load unconditional without re-reading weights).
-  const uint8_t* dummy = p.dummy + 16 * lane;
-  // weights first, so that they are in flight while the token operand stages
-  uint4 wsc_cur[FN];
-#pragma unroll
-  for (int f = 0; f < FN; ++f) wsc_cur[f] = *reinterpret_cast<const uint4*>(sptr[f]);
-  uint4 wb[kStreamDepth][FN];
-#pragma unroll
-  for (int d = 0; d < kStreamDepth; ++d) {
-#pragma unroll
-    for (int f = 0; f < FN; ++f) wb[d][f] = load_stream16(d <= last ? cptr[f] + 1024 * d : dummy);
-  }
+  // this wave's unit and K range
+  const int ui = wave / KS, kp = wave % KS;
+  const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
+  const int j = blockIdx.y * UB + ui;
+  const int per = (S + KS - 1) / KS;
+  const int sb = min(S, kp * per);
+  const int ns = min(S, sb + per) - sb;
+  const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
+                       (static_cast<int64_t>(e) * upe * S + static_cast<int64_t>(j) * S + sb) * kRecBytes;
 
-  // Stage the token operand with direct global->LDS copies (no registers):
-  // each wave copies whole rows, 1 KB of codes / 256 B of scales per
-  // instruction, and waits for its copies before the barrier.  Rows past
-  // nrows are zero-filled.
-  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, MODE == 1 ? s_slot : nullptr);
-  __syncthreads();
+  // Source rows of the tile: lane m < nrows holds row m's.  (GEMM1's row
+  // table load goes first, so that waiting for it does not wait for weights.)
+  int slot = 0, src = 0;
+  if (MODE == 0 && lane < nrows) slot = p.perm[row0 + lane];
+  UnitStep wb[D];
+#pragma unroll
+  for (int d = 0; d < kStreamEarly; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+  if (lane < nrows) src = MODE == 0 ? slot / p.k : row0 + lane;
   {
     const uint8_t* a_codes = MODE == 0 ? p.xq_codes : p.a2_codes;
     const uint8_t* a_scales = MODE == 0 ? p.xq_scales : p.a2_scales;
     const int cbytes = K / 2, sbytes = K / 16;
     for (int m = wave; m < nrows; m += 4) {
-      const int64_t src = s_src[m];
-      copy_rows_to_lds<16>(a_codes + src * cbytes, lc + m * cpitch, cbytes, lane);
-      copy_rows_to_lds<4>(a_scales + src * sbytes, ls + m * spitch, sbytes, lane);
+      const int64_t sm = __builtin_amdgcn_readlane(src, m);
+      copy_rows_to_lds<16>(a_codes + sm * cbytes, lc + m * cpitch, cbytes, lane);
+      copy_rows_to_lds<4>(a_scales + sm * sbytes, ls + m * spitch, sbytes, lane);
     }
-    for (int it = threadIdx.x; it < (MT - nrows) * (cbytes / 16); it += 256) {
-      const int m = nrows + it / (cbytes / 16), j = it % (cbytes / 16);
-      *reinterpret_cast<uint4*>(lc + m * cpitch + 16 * j) = make_uint4(0, 0, 0, 0);
-    }
-    for (int it = threadIdx.x; it < (MT - nrows) * (sbytes / 4); it += 256) {
-      const int m = nrows + it / (sbytes / 4), j = it % (sbytes / 4);
-      *reinterpret_cast<uint32_t*>(ls + m * spitch + 4 * j) = 0u;
-    }
+    // Rows past nrows are left as they are: they only feed output columns
+    // that are never stored.
     __builtin_amdgcn_s_waitcnt(0);
   }
-
-  f32x4 acc[FN][FM];
 #pragma unroll
-  for (int f = 0; f < FN; ++f)
+  for (int d = kStreamEarly; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+  // Row scales for the epilogue (used after the loop, so these loads do not
+  // hold up the first steps).
+  float grow = 1.0f;
+  if (lane < nrows) {
+    grow = MODE == 0 ? p.xq_g[src] : p.a2_g[src];
+    if (MODE == 1 && !p.deterministic) slot = p.perm[row0 + lane];
+  }
+
+  f32x4 acc[kUnitFrags][FM];
+#pragma unroll
+  for (int f = 0; f < kUnitFrags; ++f)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();  // token operand staged
 
-  for (int s8 = 0; s8 < nsteps; s8 += 8) {
-    // scales of the next 8 steps (one 16-byte load per fragment row)
-    uint4 wsc_nxt[FN];
-    const bool more = s8 + 8 <= last;
+  for (int s0 = 0; s0 < ns; s0 += D) {
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
-      wsc_nxt[f] = *reinterpret_cast<const uint4*>(more ? sptr[f] + 1024 * ((s8 + 8) / 8) : dummy);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int s = s8 + d;
-      constexpr int kSlots = kStreamDepth;
-      const int slot = d % kSlots;
-      if (s < nsteps) {
-        uint4 bc[FM];
-        half2v bsc[FM][2];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int r = fm * 16 + r16;
-          bc[fm] = *reinterpret_cast<const uint4*>(lc + r * cpitch + 64 * s + 16 * g);
-          const uint32_t sw = *reinterpret_cast<const uint16_t*>(ls + r * spitch + 8 * s + 2 * g);
-          bsc[fm][0] = e4m3_to_half2(sw);
-          bsc[fm][1] = e4m3_to_half2(sw >> 8);
-        }
-        half2v wsc[FN][2];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const uint32_t w16 = word_of(wsc_cur[f], d >> 1) >> (16 * (d & 1));
-          wsc[f][0] = e4m3_to_half2(w16);
-          wsc[f][1] = e4m3_to_half2(w16 >> 8);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          half8 bq[FM];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) bq[fm] = dequant8_f16(word_of(bc[fm], q), bsc[fm][q >> 1]);
-#pragma unroll
-          for (int f = 0; f < FN; ++f) {
-            const half8 aq = dequant8_f16(word_of(wb[slot][f], q), wsc[f][q >> 1]);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-              acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[fm], acc[f][fm], 0, 0, 0);
-          }
-        }
-      }
-      const int sn = s + kStreamDepth;
-#pragma unroll
-      for (int f = 0; f < FN; ++f) wb[slot][f] = load_stream16(sn <= last ? cptr[f] + 1024 * sn : dummy);
+    for (int d = 0; d < D; ++d) {
+      const int s = s0 + d;
+      if (s < ns) unit_step_mfma<FM>(acc, wb[d], lc, ls, cpitch, spitch, sb + s, g, r16);
+      // keep the refill of this slot after its use (no extra register set)
+      __builtin_amdgcn_sched_barrier(0);
+      const int sn = s + D;
+      load_unit_step(wb[d], sn < ns ? rec + static_cast<int64_t>(sn) * kRecBytes : p.dummy, lane);
     }
-#pragma unroll
-    for (int f = 0; f < FN; ++f) wsc_cur[f] = wsc_nxt[f];
   }
 
+  if constexpr (KS > 1) {
+    // add the K-range partials of the waves that share a unit
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();  // staged operand no longer read
+    if (kp > 0) {
+#pragma unroll
+      for (int f = 0; f < kUnitFrags; ++f)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[(((wave * kUnitFrags + f) * FM + fm) * 4 + i) * kWave + lane] = acc[f][fm][i];
+    }
+    __syncthreads();
+    if (kp == 0) {
+#pragma unroll
+      for (int o = 1; o < KS; ++o)
+#pragma unroll
+        for (int f = 0; f < kUnitFrags; ++f)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[f][fm][i] += red[((((wave + o) * kUnitFrags + f) * FM + fm) * 4 + i) * kWave + lane];
+    }
+  }
+
+  float ginv[FM];
+  int slots[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    ginv[fm] = 1.0f / __shfl(grow, fm * 16 + r16, kWave);
+    slots[fm] = __shfl(slot, fm * 16 + r16, kWave);
+  }
   if (MODE == 0) {
-    g1_epilogue<FM, FNH>(p, reinterpret_cast<const f32x4(&)[2 * FNH][FM]>(acc), e, row0, nrows,
-                         cbase, s_ginv, s_aux, wave, g, r16);
-    g1_store_band_amax<MT>(p, s_aux, row0, nrows);
-  } else {
-    g2_epilogue<FM, FN>(p, acc, e, row0, nrows, cbase, s_ginv, s_slot, g, r16);
+    if (kp == 0) {
+      g1_epilogue<FM, 2>(p, acc, e, row0, nrows, 32 * j, ginv, s_amax, wave, g, r16);
+    } else {
+      if (g == 0)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
+    }
+    g1_store_band_amax<MT>(p, s_amax, row0, nrows);
+  } else if (kp == 0) {
+    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (many rows per expert: prefill).  64-row tiles; the token
-// operand is staged in LDS as fp16 in K chunks of 256; each wave streams FN
-// weight fragments of 16 rows per chunk.
+// operand is staged in LDS as fp16 in K chunks of 256; each wave streams the
+// records of one weight unit (4 fragments of 16 rows) per chunk.
 // ---------------------------------------------------------------------------
 constexpr int kTiledKC = 256;
 constexpr int kTiledPitch = kTiledKC + 8;  // fp16 elements per LDS row (16-byte pad)
 
-template <int FM, int FN, int MODE>
+// Rows of the token operand for local row m of a tile: GEMM1 reads the
+// per-token quantized activations of token perm[row] / k, GEMM2 the
+// re-quantized activation of the expanded row itself.
+template <int MODE>
+__device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrows, int mt,
+                                          int* s_src, float* s_ginv, int* s_slot) {
+  if (static_cast<int>(threadIdx.x) < mt) {
+    const int m = threadIdx.x;
+    int src = -1, slot = -1;
+    float gi = 0.0f;
+    if (m < nrows) {
+      slot = p.perm[row0 + m];
+      src = MODE == 0 ? slot / p.k : row0 + m;
+      gi = 1.0f / (MODE == 0 ? p.xq_g[src] : p.a2_g[src]);
+    }
+    s_src[m] = src;
+    s_ginv[m] = gi;
+    s_slot[m] = slot;
+  }
+}
+
+template <int FM, int MODE>
 __global__ __launch_bounds__(256) void moe_tiled_kernel(FwdParams p) {
   constexpr int MT = 16 * FM;
-  constexpr int FNH = FN / 2;
   __shared__ _Float16 lds[MT][kTiledPitch];
   __shared__ int s_src[MT];
   __shared__ int s_slot[MT];
@@ -370,53 +398,27 @@ __global__ __launch_bounds__(256) void moe_tiled_kernel(FwdParams p) {
   const int K = MODE == 0 ? p.H : p.I;
   const uint8_t* a_codes = MODE == 0 ? p.xq_codes : p.a2_codes;
   const uint8_t* a_scales = MODE == 0 ? p.xq_scales : p.a2_scales;
-  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, MODE == 1 ? s_slot : nullptr);
+  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, s_slot);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4, r16 = lane & 15;
-  // fragment f = 16 weight rows = one 16-row group of the fragment-major copy
-  const int S = ksteps(K), Q = sgroups(K);
-  const uint8_t* cptr[FN];
-  const uint8_t* sptr[FN];
-  int cbase;
-  if (MODE == 0) {
-    cbase = blockIdx.y * (64 * FNH) + wave * 16 * FNH;
+  const int S = ksteps(K);
+  const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
+  const int j = blockIdx.y * 4 + wave;
+  const bool has_unit = j < upe;  // the last band of units may be partial
+  const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
+                       (static_cast<int64_t>(e) * upe + (has_unit ? j : 0)) * S * kRecBytes;
+  f32x4 acc[kUnitFrags][FM];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t n = f < FNH ? cbase + f * 16 : p.I + cbase + (f - FNH) * 16;
-      const int64_t grp = (static_cast<int64_t>(e) * 2 * p.I + n) / 16;
-      cptr[f] = p.w13c + grp * S * 1024 + 16 * lane;
-      sptr[f] = p.w13s + grp * Q * 1024 + 16 * lane;
-    }
-  } else {
-    cbase = blockIdx.y * (64 * FN) + wave * 16 * FN;
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int64_t grp = (static_cast<int64_t>(e) * p.H + cbase + f * 16) / 16;
-      cptr[f] = p.w2c + grp * S * 1024 + 16 * lane;
-      sptr[f] = p.w2s + grp * Q * 1024 + 16 * lane;
-    }
-  }
-  f32x4 acc[FN][FM];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
+  for (int f = 0; f < kUnitFrags; ++f)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int kc = 0; kc < K; kc += kTiledKC) {
     const int nsteps = min(kTiledKC, K - kc) / 128;
-    uint4 wb[2][FN];
-    uint32_t wsb[2][FN];
-    const int s0 = kc / 128;  // even: both steps of the chunk are in one scale group
+    const int s0 = kc / 128;
+    UnitStep wb[2];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const uint4 sg = *reinterpret_cast<const uint4*>(sptr[f] + 1024 * (s0 / 8));
-      const uint32_t w = word_of(sg, (s0 % 8) / 2);
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        wb[d][f] = load_stream16(cptr[f] + 1024 * min(s0 + d, S - 1));
-        wsb[d][f] = w >> (16 * d);
-      }
-    }
+    for (int d = 0; d < 2; ++d) load_unit_step(wb[d], rec + static_cast<int64_t>(min(s0 + d, S - 1)) * kRecBytes, lane);
     __syncthreads();  // previous chunk consumed; row table ready
     const int items = MT * nsteps * 4;
     for (int it = threadIdx.x; it < items; it += 256) {
@@ -427,50 +429,64 @@ __global__ __launch_bounds__(256) void moe_tiled_kernel(FwdParams p) {
       if (src >= 0) {
         const uint4 cw = *reinterpret_cast<const uint4*>(a_codes + static_cast<int64_t>(src) * (K / 2) + (kc + kk) / 2);
         const uint32_t sw = *reinterpret_cast<const uint16_t*>(a_scales + static_cast<int64_t>(src) * (K / 16) + (kc + kk) / 16);
-        const half2v s0 = e4m3_to_half2(sw), s1 = e4m3_to_half2(sw >> 8);
-        dst[0] = dequant8_f16(cw.x, s0);
-        dst[1] = dequant8_f16(cw.y, s0);
-        dst[2] = dequant8_f16(cw.z, s1);
-        dst[3] = dequant8_f16(cw.w, s1);
+        const half2v s0h = e4m3_to_half2(sw), s1h = e4m3_to_half2(sw >> 8);
+        dst[0] = dequant8_f16(cw.x, s0h);
+        dst[1] = dequant8_f16(cw.y, s0h);
+        dst[2] = dequant8_f16(cw.z, s1h);
+        dst[3] = dequant8_f16(cw.w, s1h);
       } else {
         const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
         dst[0] = z; dst[1] = z; dst[2] = z; dst[3] = z;
       }
     }
     __syncthreads();
+    if (has_unit) {
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      if (d < nsteps) {
-        half2v wsc[FN][2];
+      for (int d = 0; d < 2; ++d) {
+        if (d < nsteps) {
+          half2v wsc[kUnitFrags][2];
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          wsc[f][0] = e4m3_to_half2(wsb[d][f]);
-          wsc[f][1] = e4m3_to_half2(wsb[d][f] >> 8);
-        }
+          for (int f = 0; f < kUnitFrags; ++f) {
+            const uint32_t w16 = (f < 2 ? wb[d].sc.x : wb[d].sc.y) >> (16 * (f & 1));
+            wsc[f][0] = e4m3_to_half2(w16);
+            wsc[f][1] = e4m3_to_half2(w16 >> 8);
+          }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          half8 bq[FM];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            bq[fm] = *reinterpret_cast<const half8*>(&lds[fm * 16 + r16][d * 128 + 32 * g + 8 * q]);
-#pragma unroll
-          for (int f = 0; f < FN; ++f) {
-            const half8 aq = dequant8_f16(word_of(wb[d][f], q), wsc[f][q >> 1]);
+          for (int q = 0; q < 4; ++q) {
+            half8 bq[FM];
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-              acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[fm], acc[f][fm], 0, 0, 0);
+              bq[fm] = *reinterpret_cast<const half8*>(&lds[fm * 16 + r16][d * 128 + 32 * g + 8 * q]);
+#pragma unroll
+            for (int f = 0; f < kUnitFrags; ++f) {
+              const half8 aq = dequant8_f16(word_of(wb[d].c[f], q), wsc[f][q >> 1]);
+#pragma unroll
+              for (int fm = 0; fm < FM; ++fm)
+                acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[fm], acc[f][fm], 0, 0, 0);
+            }
           }
         }
       }
     }
   }
 
+  float ginv[FM];
+  int slots[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    ginv[fm] = s_ginv[fm * 16 + r16];
+    slots[fm] = s_slot[fm * 16 + r16];
+  }
   if (MODE == 0) {
-    g1_epilogue<FM, FNH>(p, reinterpret_cast<const f32x4(&)[2 * FNH][FM]>(acc), e, row0, nrows,
-                         cbase, s_ginv, s_amax, wave, g, r16);
+    if (has_unit) {
+      g1_epilogue<FM, 2>(p, acc, e, row0, nrows, 32 * j, ginv, s_amax, wave, g, r16);
+    } else if (g == 0) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
+    }
     g1_store_band_amax<MT>(p, s_amax, row0, nrows);
-  } else {
-    g2_epilogue<FM, FN>(p, acc, e, row0, nrows, cbase, s_ginv, s_slot, g, r16);
+  } else if (has_unit) {
+    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
   }
 }
 
@@ -500,60 +516,78 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-constexpr int kTiledFN = 2;
+constexpr int kTiledFM = 4;
 
 int stream_lds_bytes(int fm, int K) { return 16 * fm * ((K / 2 + 16) + (K / 16 + 4)); }
 
-// Kernel family, rows per tile and fragments per wave for a forward of T
-// tokens.  Stream kernels use 4 fragments per wave (the token operand's
-// dequantization is shared by more weight rows) when that still gives at
-// least two blocks per CU, else 2 (more, smaller blocks for tiny batches).
+static int stream_lds_total(int fm, int ks, int K) {
+  const int staged = stream_lds_bytes(fm, K);
+  const int red = ks > 1 ? 4 * kUnitFrags * fm * 4 * kWave * 4 : 0;
+  return staged > red ? staged : red;
+}
+
+// Waves that split one unit's K range: the smallest of 1, 2, 4 that gives the
+// launch at least 8 waves per CU (two per SIMD) over the units that can be
+// active, while the block's units still divide the expert's.
+static int choose_ks(int64_t units, int upe, int S) {
+  const int64_t want = 8 * 256;
+  for (int ks : {1, 2}) {
+    if ((upe % (4 / ks)) == 0 && units * ks >= want && S >= 2 * ks) return ks;
+  }
+  return 4;
+}
+
+// Kernel family, rows per tile and the K split for a forward of T tokens.
 void choose_gemm(int64_t T, FwdParams* p) {
   const int H = p->H, I = p->I, E = p->E;
   const int64_t R = T * p->k;
   const int64_t active = R < E ? R : E;
   const int64_t avg = (R + active - 1) / (active > 0 ? active : 1);
   const int Kmax = H > I ? H : I;
-  const bool bands_fit = H % 128 == 0 && I % 64 == 0;
-  if (bands_fit && avg <= 16 && stream_lds_bytes(1, Kmax) <= 65536) {
+  if (avg <= 16 && stream_lds_total(1, 4, Kmax) <= 65536) {
     p->mt = 16;
     p->gemm_kind = kGemmStream;
-  } else if (bands_fit && avg <= 32 && stream_lds_bytes(2, Kmax) <= 65536) {
+  } else if (avg <= 32 && stream_lds_total(2, 4, Kmax) <= 65536) {
     p->mt = 32;
     p->gemm_kind = kGemmStream;
   } else {
-    p->mt = 64;
+    p->mt = 16 * kTiledFM;
     p->gemm_kind = kGemmTiled;
   }
   if (p->gemm_kind == kGemmStream) {
     const int64_t tiles = (R + p->mt - 1) / p->mt > active ? (R + p->mt - 1) / p->mt : active;
-    const int64_t want = 2 * 256;
-    p->g1_fn = (I % 128 == 0 && tiles * (I / 128) >= want) ? 4 : 2;
-    p->g2_fn = (H % 256 == 0 && tiles * (H / 256) >= want) ? 4 : 2;
-    p->g1_bands = I / (32 * p->g1_fn);
+    p->g1_ks = choose_ks(tiles * (I / 32), I / 32, ksteps(H));
+    p->g2_ks = choose_ks(tiles * (H / 64), H / 64, ksteps(I));
+    p->g1_bands = (I / 32) / (4 / p->g1_ks);
   } else {
-    p->g1_fn = p->g2_fn = kTiledFN;
-    p->g1_bands = I / (64 * (kTiledFN / 2));
+    p->g1_ks = p->g2_ks = 1;
+    p->g1_bands = (I / 32 + 3) / 4;
   }
 }
 
-template <int FM, int FN1, int FN2>
+template <int FM, int KS1, int KS2>
 static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  const int nb1 = p.I / (32 * FN1);
-  moe_stream_kernel<FM, FN1, 0><<<dim3(max_tiles, nb1), 256, stream_lds_bytes(FM, p.H), s>>>(p);
+  const int nb1 = (p.I / 32) / (4 / KS1);
+  moe_stream_kernel<FM, KS1, 0><<<dim3(max_tiles, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
   if (ev) (void)hipEventRecord(ev[2], s);
   moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-  const int nb2 = p.H / (64 * FN2);
-  moe_stream_kernel<FM, FN2, 1><<<dim3(max_tiles, nb2), 256, stream_lds_bytes(FM, p.I), s>>>(p);
+  const int nb2 = (p.H / 64) / (4 / KS2);
+  moe_stream_kernel<FM, KS2, 1><<<dim3(max_tiles, nb2), 256, stream_lds_total(FM, KS2, p.I), s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
+}
+
+template <int FM, int KS1>
+static void launch_stream_ks2(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
+  if (p.g2_ks == 1) launch_stream<FM, KS1, 1>(p, max_tiles, s, ev);
+  else if (p.g2_ks == 2) launch_stream<FM, KS1, 2>(p, max_tiles, s, ev);
+  else launch_stream<FM, KS1, 4>(p, max_tiles, s, ev);
 }
 
 template <int FM>
 static void launch_stream_fm(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  if (p.g1_fn == 4 && p.g2_fn == 4) launch_stream<FM, 4, 4>(p, max_tiles, s, ev);
-  else if (p.g1_fn == 4) launch_stream<FM, 4, 2>(p, max_tiles, s, ev);
-  else if (p.g2_fn == 4) launch_stream<FM, 2, 4>(p, max_tiles, s, ev);
-  else launch_stream<FM, 2, 2>(p, max_tiles, s, ev);
+  if (p.g1_ks == 1) launch_stream_ks2<FM, 1>(p, max_tiles, s, ev);
+  else if (p.g1_ks == 2) launch_stream_ks2<FM, 2>(p, max_tiles, s, ev);
+  else launch_stream_ks2<FM, 4>(p, max_tiles, s, ev);
 }
 
 hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s,
@@ -564,12 +598,12 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     else
       launch_stream_fm<2>(p, max_tiles, s, ev);
   } else {
-    const int nb1 = p.I / (64 * (kTiledFN / 2));
-    moe_tiled_kernel<4, kTiledFN, 0><<<dim3(max_tiles, nb1), 256, 0, s>>>(p);
+    const int nb1 = (p.I / 32 + 3) / 4;
+    moe_tiled_kernel<kTiledFM, 0><<<dim3(max_tiles, nb1), 256, 0, s>>>(p);
     if (ev) (void)hipEventRecord(ev[2], s);
     moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-    const int nb2 = p.H / (64 * kTiledFN);
-    moe_tiled_kernel<4, kTiledFN, 1><<<dim3(max_tiles, nb2), 256, 0, s>>>(p);
+    const int nb2 = (p.H / 64 + 3) / 4;
+    moe_tiled_kernel<kTiledFM, 1><<<dim3(max_tiles, nb2), 256, 0, s>>>(p);
     if (ev) (void)hipEventRecord(ev[3], s);
   }
   return hipGetLastError();

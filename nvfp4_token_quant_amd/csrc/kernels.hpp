@@ -21,28 +21,33 @@ inline int route_tokens_per_block(int64_t T) {
   return static_cast<int>(tpb > kMaxTokensPerRouteBlock ? kMaxTokensPerRouteBlock : tpb);
 }
 
-// Expert weights are kept in a fragment-major layout so that one wave load
-// reads 1 KB of contiguous memory.  A weight matrix [N, K] (N % 16 == 0,
-// K % 128 == 0; the experts' matrices stacked along N) is cut into 16-row
-// groups i and 128-wide K steps s:
-//   codes:  block (i, s) = 1 KB at ((i * steps(K) + s) * 1024); lane l of a
-//           wave owns bytes [16 l, 16 l + 16) = row 16 i + l % 16, code bytes
-//           [64 s + 16 (l / 16), + 16) of that row (32 codes, k = 128 s +
-//           32 (l / 16) + 0..31).
-//   scales: block (i, q) = 1 KB at ((i * sgroups(K) + q) * 1024) for steps
-//           8 q .. 8 q + 7; lane l owns 16 bytes: for step 8 q + t the two
-//           E4M3 bytes of blocks 8 s + 2 (l / 16) + {0, 1} of row 16 i + l % 16
-//           at bytes 2 t, 2 t + 1 (zero past the last step).
+// Expert weights are re-laid out once at bind time into unit records, so that
+// a wave that owns one unit reads one contiguous 4.5 KB piece per K step.
+// A unit is four 16-row fragments of one expert's matrix: for W13 [2I, H]
+// unit j holds gate rows 32j..32j+31 (fragments 0, 1) and the matching up
+// rows I+32j..I+32j+31 (fragments 2, 3); for W2 [H, I] unit j holds rows
+// 64j..64j+63.  Record (u, s) for unit u and 128-wide K step s sits at
+// (u * ksteps(K) + s) * kRecBytes:
+//   bytes [1024 f + 16 l, + 16): lane l of fragment f = row 16 f' + l % 16
+//     of the fragment, code bytes [64 s + 16 (l / 16), + 16) of that row
+//     (32 codes, k = 128 s + 32 (l / 16) + 0..31);
+//   bytes [4096 + 8 l + 2 f, + 2): the two E4M3 scales of that lane's 32
+//     codes (blocks 8 s + 2 (l / 16) + {0, 1}).
+constexpr int kUnitFrags = 4;
+constexpr int kRecCodeBytes = 4096;
+constexpr int kRecBytes = kRecCodeBytes + 512;
 __host__ __device__ constexpr int ksteps(int K) { return K / 128; }
-__host__ __device__ constexpr int sgroups(int K) { return (K / 128 + 7) / 8; }
-__host__ __device__ constexpr int64_t packed_scale_bytes(int64_t rows, int K) {
-  return rows / 16 * sgroups(K) * 1024;
+__host__ __device__ constexpr int64_t w13_units(int64_t E, int64_t I) { return E * (I / 32); }
+__host__ __device__ constexpr int64_t w2_units(int64_t E, int64_t H) { return E * (H / 64); }
+__host__ __device__ constexpr int64_t packed_bytes(int64_t units, int K) {
+  return units * ksteps(K) * kRecBytes;
 }
 
 // Grouped-GEMM kernel families.
 //   stream: tiles of up to 16*fm rows (fm = 1, 2); the whole token operand of
-//           the tile is staged once in LDS as FP4 codes + scales, and each
-//           wave streams its weight rows with a 4-step register prefetch.
+//           the tile is staged once in LDS as FP4 codes + scales; each wave
+//           streams the records of one unit (or a K range of it) with a
+//           register prefetch.
 //   tiled:  64-row tiles; token operand staged in K chunks as fp16.
 enum GemmKind { kGemmStream = 0, kGemmTiled = 1 };
 
@@ -50,7 +55,7 @@ struct FwdParams {
   int T, H, I, E, k, R;
   int mt;             // rows per M-tile of the grouped GEMMs
   int gemm_kind;      // GemmKind
-  int g1_fn, g2_fn;   // stream kernels: 16-row weight fragments per wave
+  int g1_ks, g2_ks;   // stream kernels: waves sharing one unit's K range (1, 2, 4)
   int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
   // caller tensors
@@ -75,20 +80,18 @@ struct FwdParams {
   uint32_t* ticket;     // device scalar, 0 between launches
   // intermediates
   float* act;       // [R, I]
-  float* act_amax;  // [R, I / 64] partial row amax per GEMM1 column band
+  float* act_amax;  // [R, g1_bands <= I / 32] partial row amax per GEMM1 column band
   uint8_t* a2_codes;
   uint8_t* a2_scales;
   float* a2_g;
   float* y;        // [R, H] (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
-  // weights, fragment-major copies (see ksteps / sgroups)
-  const uint8_t* w13c;
-  const uint8_t* w13s;
+  // weights: unit records (see kRecBytes) and per-expert global scales
+  const uint8_t* w13;
   const float* w13g;
-  const uint8_t* w2c;
-  const uint8_t* w2s;
+  const uint8_t* w2;
   const float* w2g;
-  const uint8_t* dummy;  // 1 KB of zeros: target of loads past the last K step
+  const uint8_t* dummy;  // kRecBytes of zeros: target of loads past a wave's last K step
 };
 
 // quantize.hip
@@ -111,12 +114,11 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
 // events: NULL or 5 events recorded around the four kernels.
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* events);
-// Copy row-major codes [rows, K/2] / scales [rows, K/16] into the
-// fragment-major layout (rows % 16 == 0, K % 128 == 0).
-hipError_t launch_pack_codes(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                             hipStream_t s);
-hipError_t launch_pack_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                              hipStream_t s);
+// Copy row-major codes [E, N, K/2] and scales [E, N, K/16] of one weight
+// matrix into unit records.  w13: N = 2I, split = 1 (gate / up halves);
+// w2: N = H, split = 0.  N % 64 == 0, K % 128 == 0.
+hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, uint8_t* dst,
+                               int64_t E, int64_t N, int64_t K, int split, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 

@@ -85,10 +85,8 @@ struct moe_workspace {
   bool bound;
   const void* bound_w13c;  // caller's code pointers at bind time
   const void* bound_w2c;
-  uint8_t* w13c;  // fragment-major copies
-  uint8_t* w2c;
-  uint8_t* w13s;
-  uint8_t* w2s;
+  uint8_t* w13;  // unit-record copies of codes + scales
+  uint8_t* w2;
   float* w13g;
   float* w2g;
   uint8_t* dummy;
@@ -105,7 +103,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   const moe_config& c = w->cfg;
   const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, k = c.top_k;
   const int64_t R = T * k;
-  const int64_t n_amax = I / 64;  // GEMM1 column bands of 64 (the finest band used)
+  const int64_t n_amax = I / 32;  // GEMM1 column bands of 32 (the finest band used)
   const bool det = (c.flags & MOE_DETERMINISTIC_FINALIZE) != 0;
   f(reinterpret_cast<void**>(&w->xq_codes), T * H / 2);
   f(reinterpret_cast<void**>(&w->xq_scales), T * H / 16);
@@ -128,13 +126,11 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->a2_g), R * 4);
   f(reinterpret_cast<void**>(&w->y), det ? R * H * 4 : 0);
   f(reinterpret_cast<void**>(&w->out_acc), det ? 0 : T * H * 4);
-  f(reinterpret_cast<void**>(&w->w13c), E * 2 * I * H / 2);
-  f(reinterpret_cast<void**>(&w->w2c), E * H * I / 2);
-  f(reinterpret_cast<void**>(&w->w13s), nvfp4::packed_scale_bytes(E * 2 * I, static_cast<int>(H)));
-  f(reinterpret_cast<void**>(&w->w2s), nvfp4::packed_scale_bytes(E * H, static_cast<int>(I)));
+  f(reinterpret_cast<void**>(&w->w13), nvfp4::packed_bytes(nvfp4::w13_units(E, I), static_cast<int>(H)));
+  f(reinterpret_cast<void**>(&w->w2), nvfp4::packed_bytes(nvfp4::w2_units(E, H), static_cast<int>(I)));
   f(reinterpret_cast<void**>(&w->w13g), E * 4);
   f(reinterpret_cast<void**>(&w->w2g), E * 4);
-  f(reinterpret_cast<void**>(&w->dummy), 1024);
+  f(reinterpret_cast<void**>(&w->dummy), nvfp4::kRecBytes);
 }
 
 void free_all(moe_workspace* w) {
@@ -168,18 +164,18 @@ int check_weights_desc(const moe_workspace* ws, const moe_nvfp4_weights* w, bool
   return NVFP4_OK;
 }
 
-// Copy codes and scales into the library's fragment-major buffers (same
+// Copy codes and scales into the library's unit-record buffers (same
 // addresses on every call) and the global scales into their own buffers.
 hipError_t copy_weights(moe_workspace* ws, const moe_nvfp4_weights* w, const void* w13c,
                         const void* w2c, hipStream_t s) {
   const moe_config& c = ws->cfg;
   const int64_t E = c.num_experts, H = c.hidden, I = c.inter;
-  hipError_t e = nvfp4::launch_pack_codes(static_cast<const uint8_t*>(w13c), ws->w13c, E * 2 * I, H, s);
-  if (e == hipSuccess) e = nvfp4::launch_pack_codes(static_cast<const uint8_t*>(w2c), ws->w2c, E * H, I, s);
+  hipError_t e = nvfp4::launch_pack_weights(static_cast<const uint8_t*>(w13c),
+                                            static_cast<const uint8_t*>(w->w13_scales), ws->w13, E,
+                                            2 * I, H, 1, s);
   if (e == hipSuccess)
-    e = nvfp4::launch_pack_scales(static_cast<const uint8_t*>(w->w13_scales), ws->w13s, E * 2 * I, H, s);
-  if (e == hipSuccess)
-    e = nvfp4::launch_pack_scales(static_cast<const uint8_t*>(w->w2_scales), ws->w2s, E * H, I, s);
+    e = nvfp4::launch_pack_weights(static_cast<const uint8_t*>(w2c), static_cast<const uint8_t*>(w->w2_scales),
+                                   ws->w2, E, H, I, 0, s);
   if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w13_gscale, ws->w13g, E, s);
   if (e == hipSuccess) e = nvfp4::launch_copy_f32(w->w2_gscale, ws->w2g, E, s);
   return e;
@@ -289,7 +285,7 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = nvfp4::launch_fill_u32(w->ticket, 1, 0u, s);
-  if (e == hipSuccess) e = nvfp4::launch_fill_u32(reinterpret_cast<uint32_t*>(w->dummy), 256, 0u, s);
+  if (e == hipSuccess) e = nvfp4::launch_fill_u32(reinterpret_cast<uint32_t*>(w->dummy), nvfp4::kRecBytes / 4, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     free_all(w);
@@ -380,11 +376,9 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.a2_g = ws->a2_g;
   p.y = ws->y;
   p.out_acc = ws->out_acc;
-  p.w13c = ws->w13c;
-  p.w13s = ws->w13s;
+  p.w13 = ws->w13;
   p.w13g = ws->w13g;
-  p.w2c = ws->w2c;
-  p.w2s = ws->w2s;
+  p.w2 = ws->w2;
   p.w2g = ws->w2g;
   p.dummy = ws->dummy;
   const int64_t max_tiles = tiles_bound(p.R, E, p.mt);

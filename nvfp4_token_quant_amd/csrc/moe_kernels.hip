@@ -94,12 +94,16 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
                                  int32_t* __restrict__ lds_ids, int lane) {
   // Unconditional loads (index clamped; invalid candidates get key 0) so
   // that all of them are in flight at once.
+  float v[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) v[i] = lrow[min(lane + kWave * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) keep_issued(v[i]);
   uint64_t cand[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + kWave * i;
-    const float v = lrow[e < E ? e : E - 1];
-    cand[i] = e < E ? route_key(v, e) : 0ull;
+    cand[i] = e < E ? route_key(v[i], e) : 0ull;
   }
   uint64_t mine = 0, top = 0;
   for (int j = 0; j < k; ++j) {
@@ -280,12 +284,16 @@ constexpr int kSmallWaves = kSmallThreads / 64;
 template <int KPL>
 __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k, int gl,
                                     int& my_id, float& my_w) {
+  float v[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) v[i] = lrow[min(gl + 16 * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) keep_issued(v[i]);
   uint64_t cand[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int e = gl + 16 * i;
-    const float v = lrow[e < E ? e : E - 1];
-    cand[i] = e < E ? route_key(v, e) : 0ull;
+    cand[i] = e < E ? route_key(v[i], e) : 0ull;
   }
   uint64_t mine = 0, top = 0;
   for (int j = 0; j < k; ++j) {
@@ -459,44 +467,49 @@ __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Weight packing into the fragment-major layout (see kernels.hpp).  One
-// thread per 16-byte destination chunk.
+// Weight packing into unit records (layout in kernels.hpp).  One thread per
+// 16-byte destination chunk: chunks 0..255 of a record are code pieces, 256..287
+// hold the scale bytes of two lanes each.
 // ---------------------------------------------------------------------------
-__global__ void pack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                  int64_t rows, int K) {
-  const int S = ksteps(K);
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= rows / 16 * S * 64) return;
-  const int l = static_cast<int>(c & 63);
-  const int64_t is = c >> 6;
-  const int64_t i = is / S;
-  const int st = static_cast<int>(is - i * S);
-  const int64_t row = 16 * i + (l & 15);
-  const uint4 v = *reinterpret_cast<const uint4*>(src + row * (K / 2) + 64 * st + 16 * (l >> 4));
-  *reinterpret_cast<uint4*>(dst + c * 16) = v;
+__device__ __forceinline__ int64_t unit_fragment_row(int64_t u, int f, int64_t N, int split) {
+  const int64_t upe = N / 64;  // units per expert: 32 gate + 32 up rows, or 64 rows
+  const int64_t e = u / upe, j = u - e * upe;
+  const int64_t r = split ? (f < 2 ? 32 * j + 16 * f : N / 2 + 32 * j + 16 * (f - 2)) : 64 * j + 16 * f;
+  return e * N + r;
 }
 
-__global__ void pack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                   int64_t rows, int K) {
-  const int S = ksteps(K), Q = sgroups(K);
+__global__ void pack_weights_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                    uint8_t* __restrict__ dst, int64_t units, int64_t N, int K,
+                                    int split) {
+  constexpr int kChunks = kRecBytes / 16;
+  const int S = ksteps(K);
   const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= rows / 16 * Q * 64) return;
-  const int l = static_cast<int>(c & 63);
-  const int64_t iq = c >> 6;
-  const int64_t i = iq / Q;
-  const int q = static_cast<int>(iq - i * Q);
-  const int64_t row = 16 * i + (l & 15);
-  const int g = l >> 4;
-  uint8_t out[16];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int st = 8 * q + t;
-    const bool ok = st < S;
-    out[2 * t] = ok ? src[row * (K / 16) + 8 * st + 2 * g] : 0;
-    out[2 * t + 1] = ok ? src[row * (K / 16) + 8 * st + 2 * g + 1] : 0;
-  }
+  if (c >= units * S * kChunks) return;
+  const int64_t rec = c / kChunks;
+  const int w = static_cast<int>(c - rec * kChunks);
+  const int64_t u = rec / S;
+  const int s = static_cast<int>(rec - u * S);
   uint4 v;
-  __builtin_memcpy(&v, out, 16);
+  if (w < kRecCodeBytes / 16) {
+    const int f = w / 64, l = w % 64;
+    const int64_t row = unit_fragment_row(u, f, N, split) + (l & 15);
+    v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * s + 16 * (l >> 4));
+  } else {
+    uint8_t out[16];
+    const int l0 = 2 * (w - kRecCodeBytes / 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int l = l0 + h;
+#pragma unroll
+      for (int f = 0; f < kUnitFrags; ++f) {
+        const int64_t row = unit_fragment_row(u, f, N, split) + (l & 15);
+        const uint8_t* src = scales + row * (K / 16) + 8 * s + 2 * (l >> 4);
+        out[8 * h + 2 * f] = src[0];
+        out[8 * h + 2 * f + 1] = src[1];
+      }
+    }
+    __builtin_memcpy(&v, out, 16);
+  }
   *reinterpret_cast<uint4*>(dst + c * 16) = v;
 }
 
@@ -505,17 +518,12 @@ __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict
   if (i < n) dst[i] = src[i];
 }
 
-hipError_t launch_pack_codes(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                             hipStream_t s) {
-  const int64_t n = rows / 16 * ksteps(static_cast<int>(K)) * 64;
-  pack_codes_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(src, dst, rows, static_cast<int>(K));
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
-                              hipStream_t s) {
-  const int64_t n = rows / 16 * sgroups(static_cast<int>(K)) * 64;
-  pack_scales_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(src, dst, rows, static_cast<int>(K));
+hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, uint8_t* dst,
+                               int64_t E, int64_t N, int64_t K, int split, hipStream_t s) {
+  const int64_t units = E * (N / 64);
+  const int64_t n = units * ksteps(static_cast<int>(K)) * (kRecBytes / 16);
+  pack_weights_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      codes, scales, dst, units, N, static_cast<int>(K), split);
   return hipGetLastError();
 }
 
