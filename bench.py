@@ -4,11 +4,15 @@ One step = one forward of the whole layer (per-token quantize, router top-k,
 expandInputRows permutation, GEMM1 + SwiGLU, re-quantization + GEMM2,
 finalize) over one batch of seeded synthetic tokens already resident in HBM.
 Default workload: the decode-shaped layer (T=64, H=2048, E=128, top-8,
-I=768).  Prints one JSON line.
+I=768).  `--layer 4` times the quantize-only workload instead (per-token
+NVFP4 quantization of x bf16 [16384, 7168]; one step = one launch).  Prints
+one JSON line.
 
 Timing: `steps` forwards after `warmup` untimed ones, bracketed by
-synchronizations; wall time gives `value` (tokens/s).  Every timed forward
-also records HIP events around its four kernels on its own stream, which give
+synchronizations; wall time gives `value` (tokens/s).  By default each timed
+forward is replayed from its own captured HIP graph (as decode serving does;
+`--eager` launches the kernels directly), back to back.  Every timed forward
+records HIP events around its four kernels on its own stream, which give
 each kernel's mean duration; the dominant kernel's algorithmic bytes (or
 FLOPs) over that duration is `roofline.achieved`.  Expert weights rotate over
 `--rotate` copies so consecutive steps do not find them in the 256 MB
@@ -34,15 +38,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layer", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--layer", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the layer's)")
     ap.add_argument("--fast-finalize", action="store_true",
                     help="atomic (non-deterministic) finalize instead of the slot-ordered one")
     ap.add_argument("--rotate", type=int, default=2, help="copies of the expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="replay each timed forward from a captured HIP graph (as decode serving does)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the kernels directly instead of replaying captured HIP graphs")
     return ap.parse_args()
 
 
@@ -82,6 +86,8 @@ def main():
     from nvfp4_token_quant_amd.workloads import gpu_weights, to_device_bf16
 
     binding.lib()  # fails loudly if the HIP library is missing
+    if args.layer == 4:
+        return bench_quantize(args)
     L = synth.LAYERS[args.layer]
     T = args.T or L.T
     H, I, E, k = L.H, L.I, L.E, L.k
@@ -134,40 +140,31 @@ def main():
     torch.cuda.synchronize()
     lib = binding.lib()
     lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
-    if args.graph:
-        # one graph per weight copy; the stage events are recorded inside the
-        # graph, so every replay re-records them on the replay stream
-        nrot = len(layers)
-        evs = [[hip.event() for _ in range(5)] for _ in range(nrot)]
+    if not args.eager:
+        # one captured graph per timed forward, each with its own stage events
+        # (recorded inside the graph, so every replay re-records them)
+        evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            for r, ly in enumerate(layers):
-                lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in evs[r]]))
+            for i in range(args.steps):
+                ly = layers[i % len(layers)]
+                lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in evs[i]]))
+                # record the events once outside the graph (HIP reports no elapsed
+                # time for events that were only ever recorded by graph nodes)
                 ly.forward_into(x, logits, out)
-                torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     ly.forward_into(x, logits, out)
                 graphs.append(g)
         torch.cuda.synchronize()
-        per_stage = {s: [] for s in stages}
-        t_total = 0.0
-        for i in range(args.steps):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graphs[i % nrot].replay()
-            torch.cuda.synchronize()
-            t_total += time.perf_counter() - t0
-            step = evs[i % nrot]
-            for j, s in enumerate(stages):
-                per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
-        # back-to-back replays for the wall-clock throughput
+        for g in graphs[: min(len(graphs), args.warmup)]:
+            g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % nrot].replay()
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     else:
@@ -181,10 +178,10 @@ def main():
             ly.forward_into(x, logits, out)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        per_stage = {s: [] for s in stages}
-        for step in evs:
-            for j, s in enumerate(stages):
-                per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
+    per_stage = {s: [] for s in stages}
+    for step in evs:
+        for j, s in enumerate(stages):
+            per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
     for ly in layers:
         lib.moe_workspace_set_stage_events(ly.handle, None)
     mean_ms = {s: float(np.mean(v)) for s, v in per_stage.items()}
@@ -233,13 +230,95 @@ def main():
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": f"nvfp4_moe_layer_{L.name}", "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
-                   "weights_rotated": args.rotate, "hip_graph": bool(args.graph),
+                   "weights_rotated": args.rotate, "hip_graph": not args.eager,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def bench_quantize(args):
+    """Quantize-only workload: one step = one nvfp4_quantize_per_token launch
+    over x bf16 [T, H] (read 2 B, write 0.5625 B per element + 4 B per row)."""
+    import numpy as np
+    import torch
+
+    from nvfp4_token_quant_amd import binding, synth
+    from nvfp4_token_quant_amd.workloads import to_device_bf16
+
+    L = synth.LAYERS[4]
+    T = args.T or L.T
+    H = L.H
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: layer 4 ({L.name}) T={T} H={H}", file=sys.stderr, flush=True)
+    x_bits = synth.activations(4, T)
+    nrot = max(1, args.rotate)
+    xs = [to_device_bf16(x_bits, dev) for _ in range(nrot)]
+    outs = [(torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T, H // 16), dtype=torch.uint8, device=dev),
+             torch.empty((T,), dtype=torch.float32, device=dev)) for _ in range(nrot)]
+    for i in range(args.warmup):
+        binding.quantize_per_token_into(xs[i % nrot], *outs[i % nrot])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        binding.quantize_per_token_into(xs[i % nrot], *outs[i % nrot])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = T * H * 2 + T * H // 2 + T * H // 16 + 4 * T
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_quantize(args, x_bits)
+    result = {
+        "metric": "NVFP4 MoE layer tokens/s + % roofline (HBM GB/s decode, MFMA prefill)",
+        "value": T * args.steps / (t1 - t0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 in; e2m1 + e4m3 + f32 out)",
+        "data": "synthetic (seeded Student-t(3) rows, every 97th row zero, 4 rows x1e3)",
+        "config": {"workload": "nvfp4_quantize_per_token", "layer_id": 4, "T": T, "H": H,
+                   "inputs_rotated": nrot, "hip_graph": False, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "quantize_rows",
+                     "kernel_ms": kernel_ms, "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_quantize(args, x_bits):
+    """The oracle's per-row quantizer, as it stands, on a bounded sample of rows."""
+    import oracle
+
+    T = x_bits.shape[0]
+    n = min(T, 256)
+    oracle.quantize_rows(x_bits[:n])
+    t0 = time.perf_counter()
+    oracle.quantize_rows(x_bits[:n])
+    per_row = (time.perf_counter() - t0) / n
+    n = int(min(T, max(n, args.cpu_budget_s / max(per_row, 1e-9))))
+    reps, dt = 0, 0.0
+    while dt < args.cpu_budget_s * 0.8 or reps == 0:
+        t0 = time.perf_counter()
+        oracle.quantize_rows(x_bits[:n])
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {T} rows x {reps} repetitions ({dt:.1f} s)"}
 
 
 def cpu_baseline(args, x_bits, T, H, I, k):

@@ -152,6 +152,18 @@ def quantize_per_token(x: torch.Tensor, stream=None):
     return codes, scales, g
 
 
+def quantize_per_token_into(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                            g: torch.Tensor, stream=None):
+    """quantize_per_token into caller-owned outputs (no allocation)."""
+    _require(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    _check(lib().nvfp4_quantize_per_token(_ptr(x), rows, cols, x.stride(0) if rows else cols,
+                                          _ptr(codes), _ptr(scales), _ptr(g), _stream(stream)))
+    return codes, scales, g
+
+
 def quantize_experts(w: torch.Tensor, stream=None):
     """w f32 [E, rows, cols] -> (codes [E, rows, cols/2], scales [E, rows, cols/16], g [E])."""
     _require(w, torch.float32, "w")

@@ -149,7 +149,7 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
 // at the end).  The tile's token operand is staged once in LDS as FP4 codes +
 // E4M3 scales (dynamic LDS: MT rows x (K/2 + 16) code bytes and (K/16 + 4)
 // scale bytes); each wave then walks its K range in 128-wide steps, one
-// 4.5 KB unit record per step, with the next kStreamDepth records in flight.
+// 4.5 KB unit record per step, with the next few records in flight.
 //
 // Issue order.  Vector loads complete in issue order, so a wait for the
 // staging copies also waits for every weight load issued before them.  The
@@ -158,10 +158,21 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
 // computing as soon as its first records land instead of after all of them.
 // Every later load is unconditional (past the wave's range it reads a zero
 // dummy record), so each wait covers exactly the oldest step.
-// MODE 0: GEMM1 (W13 units: 2 gate + 2 up fragments, SwiGLU epilogue);
-// MODE 1: GEMM2 (W2 units: 4 output fragments).
+// MODE 0: GEMM1 (W13 units: 2 gate + 2 up fragments, SwiGLU epilogue); the
+//   token operand is the per-token quantized x, copied to LDS with direct
+//   global->LDS loads.
+// MODE 1: GEMM2 (W2 units: 4 output fragments); the token operand is the
+//   re-quantization of the tile's act rows, done here: the block reads the
+//   rows' GEMM1 amax partials and the act values into registers ahead of the
+//   weight stream, then quantizes into LDS (band-0 blocks also store the
+//   result, for inspection).  All bands of a tile run on one XCD (the tile
+//   count of the grid is a multiple of 8), so the repeated act reads hit
+//   that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kStreamDepth = 5;
+template <int MODE>
+struct StreamDepth {
+  static constexpr int value = MODE == 0 ? 5 : 3;
+};
 constexpr int kStreamEarly = 2;  // steps issued before the staging copies
 
 // Copy `bytes` bytes from global memory to LDS with global_load_lds: one wave
@@ -230,13 +241,20 @@ __device__ __forceinline__ void unit_step_mfma(f32x4 (&acc)[kUnitFrags][FM], con
   }
 }
 
+// Act values of one 16-element block of an expanded row.
+struct ActBlock {
+  float4 v[4];
+};
+
 template <int FM, int KS, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3 : 2))) void moe_stream_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3 + MODE : 2))) void moe_stream_kernel(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MT = 16 * FM;
   constexpr int UB = 4 / KS;  // units per block
-  constexpr int D = kStreamDepth;
+  constexpr int D = StreamDepth<MODE>::value;
+  constexpr int kRq = 2;  // re-quantization items per thread loaded ahead of the weights
   __shared__ float s_amax[4][MT];
+  __shared__ float s_g2[MT];
   if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
   const int4 td = p.tiles[blockIdx.x];
   const int e = td.x, row0 = td.y, nrows = td.z;
@@ -258,35 +276,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
                        (static_cast<int64_t>(e) * upe * S + static_cast<int64_t>(j) * S + sb) * kRecBytes;
 
-  // Source rows of the tile: lane m < nrows holds row m's.  (GEMM1's row
-  // table load goes first, so that waiting for it does not wait for weights.)
-  int slot = 0, src = 0;
-  if (MODE == 0 && lane < nrows) slot = p.perm[row0 + lane];
+  // Rows past nrows in the LDS operand are left as they are: they only feed
+  // output columns that are never stored.
   UnitStep wb[D];
+  int slot = 0;
+  float grow = 1.0f;  // GEMM1: the row's token global scale (lane m < nrows holds row m's)
+  if constexpr (MODE == 0) {
+    // Source rows of the tile.  The row table load goes first, so that
+    // waiting for it does not wait for weights.
+    int src = 0;
+    if (lane < nrows) slot = p.perm[row0 + lane];
 #pragma unroll
-  for (int d = 0; d < kStreamEarly; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-  if (lane < nrows) src = MODE == 0 ? slot / p.k : row0 + lane;
-  {
-    const uint8_t* a_codes = MODE == 0 ? p.xq_codes : p.a2_codes;
-    const uint8_t* a_scales = MODE == 0 ? p.xq_scales : p.a2_scales;
+    for (int d = 0; d < kStreamEarly; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    if (lane < nrows) src = slot / p.k;
     const int cbytes = K / 2, sbytes = K / 16;
     for (int m = wave; m < nrows; m += 4) {
       const int64_t sm = __builtin_amdgcn_readlane(src, m);
-      copy_rows_to_lds<16>(a_codes + sm * cbytes, lc + m * cpitch, cbytes, lane);
-      copy_rows_to_lds<4>(a_scales + sm * sbytes, ls + m * spitch, sbytes, lane);
+      copy_rows_to_lds<16>(p.xq_codes + sm * cbytes, lc + m * cpitch, cbytes, lane);
+      copy_rows_to_lds<4>(p.xq_scales + sm * sbytes, ls + m * spitch, sbytes, lane);
     }
-    // Rows past nrows are left as they are: they only feed output columns
-    // that are never stored.
     __builtin_amdgcn_s_waitcnt(0);
-  }
 #pragma unroll
-  for (int d = kStreamEarly; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-  // Row scales for the epilogue (used after the loop, so these loads do not
-  // hold up the first steps).
-  float grow = 1.0f;
-  if (lane < nrows) {
-    grow = MODE == 0 ? p.xq_g[src] : p.a2_g[src];
-    if (MODE == 1 && !p.deterministic) slot = p.perm[row0 + lane];
+    for (int d = kStreamEarly; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    // the epilogue's row scales (used after the loop)
+    if (lane < nrows) grow = p.xq_g[src];
+  } else {
+    // Fused re-quantization.  Loads in issue order: GEMM1 amax partials of
+    // the wave's rows, the first kRq act blocks of this thread, then the
+    // whole weight prefetch window; each wait below covers only the loads
+    // it needs.
+    const int nbl = K / 16, nb = p.g1_bands;
+    const int items = nrows * nbl;
+    constexpr int RPW = MT / 4;  // rows per wave
+    float pa[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int m = wave + 4 * i;
+      const int64_t row = row0 + min(m, nrows - 1);
+      pa[i] = p.act_amax[row * nb + min(lane, nb - 1)];
+    }
+    ActBlock ab[kRq];
+#pragma unroll
+    for (int i = 0; i < kRq; ++i) {
+      const int it = min(static_cast<int>(threadIdx.x) + 256 * i, items - 1);
+      const int m = it / nbl, b = it - m * nbl;
+      const float4* src4 = reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(row0 + m) * K + 16 * b);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ab[i].v[q] = src4[q];
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    if (!p.deterministic && lane < nrows) slot = p.perm[row0 + lane];
+    // row global scales g2 = 2688 / amax(act row)
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int m = wave + 4 * i;
+      float a = lane < nb ? pa[i] : 0.0f;
+      for (int c = lane + kWave; c < nb; c += kWave)
+        a = fmaxf(a, p.act_amax[static_cast<int64_t>(row0 + min(m, nrows - 1)) * nb + c]);
+      a = wave_max(a);
+      if (lane == 0 && m < nrows) {
+        const float g2 = global_scale(a);
+        s_g2[m] = g2;
+        if (blockIdx.y == 0) p.a2_g[row0 + m] = g2;
+      }
+    }
+    __syncthreads();
+    auto quant_item = [&](const ActBlock& a, int it) {
+      const int m = it / nbl, b = it - m * nbl;
+      float f[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[4 * q] = a.v[q].x; f[4 * q + 1] = a.v[q].y; f[4 * q + 2] = a.v[q].z; f[4 * q + 3] = a.v[q].w;
+      }
+      uint32_t lo, hi;
+      const uint32_t sb = quantize_block16(f, s_g2[m], lo, hi);
+      *reinterpret_cast<uint2*>(lc + m * cpitch + 8 * b) = make_uint2(lo, hi);
+      ls[m * spitch + b] = static_cast<uint8_t>(sb);
+      if (blockIdx.y == 0) {
+        const int64_t row = row0 + m;
+        *reinterpret_cast<uint2*>(p.a2_codes + row * (K / 2) + 8 * b) = make_uint2(lo, hi);
+        p.a2_scales[row * (K / 16) + b] = static_cast<uint8_t>(sb);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kRq; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + 256 * i;
+      if (it < items) quant_item(ab[i], it);
+    }
+    // tiles with more items than kRq per thread: the rest, batch by batch
+    for (int base = 256 * kRq; base < items; base += 256) {
+      const int it = base + static_cast<int>(threadIdx.x);
+      if (it < items) {
+        const int m = it / nbl, b = it - m * nbl;
+        const float4* src4 = reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(row0 + m) * K + 16 * b);
+        ActBlock a;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a.v[q] = src4[q];
+        quant_item(a, it);
+      }
+    }
   }
 
   f32x4 acc[kUnitFrags][FM];
@@ -338,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   int slots[FM];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    ginv[fm] = 1.0f / __shfl(grow, fm * 16 + r16, kWave);
+    ginv[fm] = 1.0f / (MODE == 0 ? __shfl(grow, fm * 16 + r16, kWave) : s_g2[fm * 16 + r16]);
     slots[fm] = __shfl(slot, fm * 16 + r16, kWave);
   }
   if (MODE == 0) {
@@ -570,9 +659,10 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
   const int nb1 = (p.I / 32) / (4 / KS1);
   moe_stream_kernel<FM, KS1, 0><<<dim3(max_tiles, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
   if (ev) (void)hipEventRecord(ev[2], s);
-  moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
   const int nb2 = (p.H / 64) / (4 / KS2);
-  moe_stream_kernel<FM, KS2, 1><<<dim3(max_tiles, nb2), 256, stream_lds_total(FM, KS2, p.I), s>>>(p);
+  // a multiple of 8 tiles keeps every band of a tile on the same XCD
+  const int gx = (max_tiles + 7) / 8 * 8;
+  moe_stream_kernel<FM, KS2, 1><<<dim3(gx, nb2), 256, stream_lds_total(FM, KS2, p.I), s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
 }
 

@@ -436,34 +436,46 @@ static void launch_prologue_small(const FwdParams& p, hipStream_t s) {
 
 // Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[inv[t, j], n]) in slot
 // order (deterministic), or bf16_rne(out_acc[t, n]) after the atomic epilogue.
-// One thread per 8 output columns.
+// One thread per 4 output columns; the slots are taken 8 at a time with all
+// their row-index, weight and y loads issued before the sums.
 __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
   const int H = p.H, k = p.k;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int per_row = H / 8;
+  const int per_row = H / 4;
   if (idx >= static_cast<int64_t>(p.T) * per_row) return;
   const int64_t t = idx / per_row;
-  const int n = static_cast<int>(idx % per_row) * 8;
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int n = static_cast<int>(idx % per_row) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.deterministic) {
-    for (int j = 0; j < k; ++j) {
-      const float w = p.topk_w[t * k + j];
-      const float4* yr = reinterpret_cast<const float4*>(p.y + static_cast<int64_t>(p.inv[t * k + j]) * H + n);
-      const float4 a = yr[0], b = yr[1];
-      s[0] += w * a.x; s[1] += w * a.y; s[2] += w * a.z; s[3] += w * a.w;
-      s[4] += w * b.x; s[5] += w * b.y; s[6] += w * b.z; s[7] += w * b.w;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int rows[8];
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t sl = t * k + min(j0 + j, k - 1);
+        rows[j] = p.inv[sl];
+        w[j] = j0 + j < k ? p.topk_w[sl] : 0.0f;
+      }
+      float4 y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = *reinterpret_cast<const float4*>(p.y + static_cast<int64_t>(rows[j]) * H + n);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j < k) {
+          acc.x += w[j] * y[j].x;
+          acc.y += w[j] * y[j].y;
+          acc.z += w[j] * y[j].z;
+          acc.w += w[j] * y[j].w;
+        }
+      }
     }
   } else {
-    const float4* r = reinterpret_cast<const float4*>(p.out_acc + t * H + n);
-    const float4 a = r[0], b = r[1];
-    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w; s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+    acc = *reinterpret_cast<const float4*>(p.out_acc + t * H + n);
   }
-  uint4 o;
-  o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
-  o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
-  o.z = f32_to_bf16_rne(s[4]) | (f32_to_bf16_rne(s[5]) << 16);
-  o.w = f32_to_bf16_rne(s[6]) | (f32_to_bf16_rne(s[7]) << 16);
-  *reinterpret_cast<uint4*>(p.out + t * H + n) = o;
+  uint2 o;
+  o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+  o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(p.out + t * H + n) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -566,7 +578,7 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
   }
   if (ev) (void)hipEventRecord(ev[1], s);
   launch_grouped_gemms(p, max_tiles, s, ev);
-  const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 8);
+  const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 4);
   moe_finalize_kernel<<<static_cast<unsigned>((nthreads + 255) / 256), 256, 0, s>>>(p);
   if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();
