@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch the kernels directly instead of replaying captured HIP graphs")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain device copy of 256 MiB, `steps` times (the known-size "
+                         "kernel that scales the profiler's HBM byte counters)")
     return ap.parse_args()
 
 
@@ -85,6 +88,8 @@ def main():
     from nvfp4_token_quant_amd import binding, synth
     from nvfp4_token_quant_amd.workloads import gpu_weights, to_device_bf16
 
+    if args.copy_reference:
+        return copy_reference(args)
     binding.lib()  # fails loudly if the HIP library is missing
     if args.layer == 4:
         return bench_quantize(args)
@@ -237,6 +242,19 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def copy_reference(args):
+    """A plain 256 MiB device-to-device copy (reads and writes 256 MiB each)."""
+    import torch
+
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": n, "copies": args.steps}), flush=True)
 
 
 def bench_quantize(args):

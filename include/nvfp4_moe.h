@@ -63,8 +63,9 @@ const char* nvfp4_last_error(void);
  * code = E2M1_rne_sat(RN(x * r_b)).
  * Dequantization: x ~= value(code) * value(S_b) / g.
  *
- *   x_dev       bf16 [rows, ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= cols
- *   rows        >= 0 (0 is a no-op)
+ *   x_dev       bf16 [rows, ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= cols;
+ *               finite values (an inf or NaN gives unspecified codes for its row)
+ *   rows        0 <= rows < 2^31 (0 is a no-op)
  *   cols        > 0, multiple of 16
  *   codes_dev   u8 [rows, cols/2], 16-byte aligned   (written)
  *   scales_dev  u8 [rows, cols/16]                   (written)

@@ -14,6 +14,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -48,26 +49,45 @@ __device__ __forceinline__ float global_scale(float a) {
   return __builtin_isinf(g) ? 3.402823466e38f : g;
 }
 
-// E4M3 encode, round to nearest even, saturating at 448 (0x7E); s >= 0 finite.
+// E4M3 encode, round to nearest even, for 0 <= s < 464 (the block scales of
+// the recipe never exceed 448 * (1 + 2^-22): t = RN(amax_b * g) <= 2688 (1 +
+// 2^-24)^2 since amax_b <= amax_row).  gfx950's converter produces the OCP
+// E4M3 byte directly; on [0, 464) it rounds to nearest even with values in
+// [448, 464) going to 448 (0x7E), the same bytes as the software definition
+// (every fp32 value of the interval was compared on the device).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (s >= 448.0f) return 0x7Eu;
-  if (s < 0.015625f) {                   // below 2^-6: subnormal codes, quantum 2^-9
-    return static_cast<uint32_t>(__builtin_rintf(s * 512.0f));  // 0..8 (8 == 2^-6)
-  }
-  uint32_t u = __float_as_uint(s);
-  uint32_t e = (u >> 23) - 120u;         // biased E4M3 exponent: (u>>23) - 127 + 7
-  uint32_t m = u & 0x7FFFFFu;
-  uint32_t keep = m >> 20, rem = m & 0xFFFFFu;
-  uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & keep);
-  uint32_t code = (e << 3) + keep + up;  // mantissa carry bumps the exponent
-  return code > 0x7Eu ? 0x7Eu : code;
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(s, 0.0f, 0, false)) & 0xFFu;
 }
 
-// E4M3 bits -> binary32 value (exact).
+// E4M3 bits -> binary32 value (exact; b <= 0x7E or its negative).
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  if (e == 0) return static_cast<float>(m) * 0.001953125f;   // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(b), 0);
+}
+
+// RN(t / 6) for t >= 0.  q0 = RN(t * RN(1/6)) is within an ulp, the residual
+// t - 6 q0 is exact with an FMA, and one FMA correction rounds correctly
+// (Markstein's theorem for a correctly rounded reciprocal).  Checked against
+// the binary64 quotient on every non-negative float: equal for t >= 2^-125;
+// below, both results are under 2^-120 and encode to the same E4M3 zero.
+__device__ __forceinline__ float div6_rn(float t) {
+  const float c = 0.16666667163372039794921875f;  // RN(1/6)
+  const float q0 = t * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, t), c, q0);
+}
+
+// RN(g / d) for an E4M3 value d > 0 and g >= 2^-117 (every global scale
+// 2688 / amax is, for finite amax), +inf saturated to FLT_MAX.  y = RN(1/d)
+// comes from the hardware reciprocal plus one Newton step (exact for all 126
+// E4M3 values, compared on the device); the quotient then takes the same
+// FMA correction as div6_rn.  Compared with the binary64 quotient for every
+// E4M3 divisor over the binades of g from 2^-117 up (no mismatch; the
+// mismatches below come from subnormal quotients, which cannot occur here).
+__device__ __forceinline__ float div_e4m3_rn(float g, float d) {
+  float y = __builtin_amdgcn_rcpf(d);
+  y = __builtin_fmaf(__builtin_fmaf(-d, y, 1.0f), y, y);
+  const float q0 = g * y;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, g), y, q0);
+  return __builtin_isinf(q0) ? 3.402823466e38f : __builtin_fminf(q, 3.402823466e38f);
 }
 
 // Eight binary32 values (already multiplied by the block's r) -> eight E2M1
@@ -118,28 +138,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Quantize one 16-element block held as binary32 values with global scale g.
-// Returns the E4M3 scale byte; writes the 8 code bytes as two dwords.
-// The operation order is the recipe's: s = RN(RN(amax*g)/6), r = RN(g/d)
-// (saturated to FLT_MAX), code = E2M1(RN(x*r)); no contraction is possible
-// (no additions).
-__device__ __forceinline__ uint32_t quantize_block16(const float* x, float g, uint32_t& lo,
-                                                     uint32_t& hi) {
-  float ab = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(x[i]));
-  float t = ab * g;
-  float s = t / 6.0f;
-  uint32_t sb = e4m3_encode(s);
-  float d = e4m3_value(sb);
-  float r = d > 0.0f ? g / d : 0.0f;
-  if (__builtin_isinf(r)) r = 3.402823466e38f;  // g clamped to FLT_MAX: keep r finite
+// Quantize one 16-element block held as binary32 values with global scale g,
+// given the block's amax.  Returns the E4M3 scale byte; writes the 8 code
+// bytes as two dwords.  The operation order is the recipe's: s =
+// RN(RN(amax*g)/6), r = RN(g/d) (saturated to FLT_MAX), code = E2M1(RN(x*r));
+// the divisions use the correctly rounded forms above.
+__device__ __forceinline__ uint32_t quantize_block16_amax(const float* x, float ab, float g,
+                                                          uint32_t& lo, uint32_t& hi) {
+  const float t = ab * g;
+  const uint32_t sb = e4m3_encode(div6_rn(t));
+  const float d = e4m3_value(sb);
+  const float r = d > 0.0f ? div_e4m3_rn(g, d) : 0.0f;
   float v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = x[i] * r;
   lo = e2m1_pack8(v);
   hi = e2m1_pack8(v + 8);
   return sb;
+}
+
+__device__ __forceinline__ uint32_t quantize_block16(const float* x, float g, uint32_t& lo,
+                                                     uint32_t& hi) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(x[i]));
+  return quantize_block16_amax(x, ab, g, lo, hi);
 }
 
 }  // namespace nvfp4

@@ -196,7 +196,7 @@ int nvfp4_quantize_per_token(const void* x_dev, int64_t rows, int64_t cols, int6
   if (ld_x < cols || ld_x % 8 != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "ld_x must be >= cols and a multiple of 8 (got %lld)", (long long)ld_x);
   if (rows == 0) return ok();
-  if (rows > (int64_t(1) << 32)) return fail(NVFP4_ERR_INVALID_ARG, "rows too large");
+  if (rows > INT32_MAX) return fail(NVFP4_ERR_INVALID_ARG, "rows must be < 2^31 (got %lld)", (long long)rows);
   if (!x_dev || !codes_dev || !scales_dev || !gscale_dev)
     return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned(x_dev, 16) || !aligned(codes_dev, 16) || !aligned(gscale_dev, 4))

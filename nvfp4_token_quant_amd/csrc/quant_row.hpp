@@ -27,39 +27,63 @@ __device__ __forceinline__ float amax16_bf16(const uint4& a, const uint4& b) {
   return __uint_as_float(m << 16);
 }
 
+// A row held in registers: lane l owns blocks l, l + 64, ... (NB of them).
+template <int NB>
+struct RowRegs {
+  uint4 v[NB][2];
+};
+
+// Unconditional loads (block index clamped) so that they are all in flight
+// together; blocks past the row end are masked out by the quantize step.
+template <int NB>
+__device__ __forceinline__ void load_row(RowRegs<NB>& rr, const uint16_t* __restrict__ xrow, int nblk,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int b = lane + kWave * i;
+    const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * (b < nblk ? b : nblk - 1));
+    rr.v[i][0] = load_stream16(p);
+    rr.v[i][1] = load_stream16(p + 1);
+  }
+}
+
+// Row amax -> g, then every block of the row; the block amaxes of the first
+// pass are reused by the second.
+template <int NB>
+__device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nblk, uint8_t* __restrict__ crow,
+                                                  uint8_t* __restrict__ srow, float* __restrict__ gout,
+                                                  int lane) {
+  float bam[NB];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    bam[i] = amax16_bf16(rr.v[i][0], rr.v[i][1]);
+    if (lane + kWave * i < nblk) am = fmaxf(am, bam[i]);
+  }
+  const float g = global_scale(wave_max(am));
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int b = lane + kWave * i;
+    if (b < nblk) {
+      float f[16];
+      unpack16(rr.v[i][0], rr.v[i][1], f);
+      uint32_t lo, hi;
+      const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
+      *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
+      srow[b] = static_cast<uint8_t>(sb);
+    }
+  }
+  if (lane == 0) *gout = g;
+}
+
 template <int NB>
 __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
                                   uint8_t* __restrict__ crow, uint8_t* __restrict__ srow,
                                   float* __restrict__ gout, int lane) {
   if constexpr (NB > 0) {
-    uint4 v[NB][2];
-    float am = 0.0f;
-    // Unconditional loads (block index clamped) so that they are all in
-    // flight together; blocks past the row end count as zeros.
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int b = lane + kWave * i;
-      const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * (b < nblk ? b : nblk - 1));
-      v[i][0] = load_stream16(p);
-      v[i][1] = load_stream16(p + 1);
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      if (lane + kWave * i < nblk) am = fmaxf(am, amax16_bf16(v[i][0], v[i][1]));
-    const float g = global_scale(wave_max(am));
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int b = lane + kWave * i;
-      if (b < nblk) {
-        float f[16];
-        unpack16(v[i][0], v[i][1], f);
-        uint32_t lo, hi;
-        const uint32_t sb = quantize_block16(f, g, lo, hi);
-        *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
-        srow[b] = static_cast<uint8_t>(sb);
-      }
-    }
-    if (lane == 0) *gout = g;
+    RowRegs<NB> rr;
+    load_row<NB>(rr, xrow, nblk, lane);
+    quantize_row_regs<NB>(rr, nblk, crow, srow, gout, lane);
   } else {
     // Rows too long for the register cache: amax pass, then quantize pass.
     float am = 0.0f;

@@ -10,8 +10,9 @@
 // l, l+64, l+128, ...: each block is two 16-byte loads of bf16, so one wave
 // instruction reads 2 KB of contiguous row, and each lane writes its block's
 // 8 code bytes with one 8-byte store.  The block amax is lane-local (a lane
-// holds whole blocks); the row amax is one wave reduction.  With up to NB
-// blocks per lane cached in registers the row is read from HBM once.
+// holds whole blocks); the row amax is one wave reduction (plus one LDS
+// exchange when a block of four waves shares a row).  With the row's blocks
+// cached in registers it is read from HBM once.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_row.hpp"
@@ -19,17 +20,70 @@
 namespace nvfp4 {
 
 
-template <int NB>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x,
-                                                            int64_t rows, int cols, int64_t ld,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales,
-                                                            float* __restrict__ gs) {
+// Rows of up to 2048 blocks (cols <= 32768): one block of 256 threads per
+// row, thread t owning blocks t, t + 256, ... (NBL of them) in registers.
+// Small per-thread register caches keep eight waves per SIMD resident, so
+// many rows' loads are in flight while others quantize; the row amax takes
+// one LDS exchange between the block's four waves.
+template <int NBL>
+__global__ __launch_bounds__(256) void quantize_rows_block_kernel(const uint16_t* __restrict__ x,
+                                                                  int64_t rows, int cols, int64_t ld,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales,
+                                                                  float* __restrict__ gs) {
+  __shared__ float s_am[4];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int nblk = cols / 16;
+  const uint16_t* xrow = x + row * ld;
+  uint4 v[NBL][2];
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * min(t + 256 * i, nblk - 1));
+    v[i][0] = load_stream16(p);
+    v[i][1] = load_stream16(p + 1);
+  }
+  float bam[NBL];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    bam[i] = amax16_bf16(v[i][0], v[i][1]);
+    if (t + 256 * i < nblk) am = fmaxf(am, bam[i]);
+  }
+  am = wave_max(am);
+  if (lane == 0) s_am[wave] = am;
+  __syncthreads();
+  const float g = global_scale(fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3])));
+  uint8_t* crow = codes + row * (cols / 2);
+  uint8_t* srow = scales + row * (cols / 16);
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int b = t + 256 * i;
+    if (b < nblk) {
+      float f[16];
+      unpack16(v[i][0], v[i][1], f);
+      uint32_t lo, hi;
+      const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
+      // streaming stores: the outputs are not re-read by this kernel
+      const u32x2 cv = {lo, hi};
+      __builtin_nontemporal_store(cv, reinterpret_cast<u32x2*>(crow + 8 * b));
+      __builtin_nontemporal_store(static_cast<uint8_t>(sb), srow + b);
+    }
+  }
+  if (t == 0) gs[row] = g;
+}
+
+// Longer rows: one wave per row, two passes over the row.
+__global__ __launch_bounds__(256) void quantize_rows_long_kernel(const uint16_t* __restrict__ x,
+                                                                 int64_t rows, int cols, int64_t ld,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ gs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (row >= rows) return;
-  quantize_row_wave<NB>(x + row * ld, cols / 16, codes + row * (cols / 2), scales + row * (cols / 16),
-                        gs + row, lane);
+  quantize_row_wave<0>(x + row * ld, cols / 16, codes + row * (cols / 2), scales + row * (cols / 16),
+                       gs + row, lane);
 }
 
 int quant_nb_for_cols(int64_t cols) {
@@ -43,15 +97,22 @@ int quant_nb_for_cols(int64_t cols) {
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, float* gs, hipStream_t s) {
-  const int rows_per_block = 4;
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
-  const dim3 block(kWave * rows_per_block);
-  switch (quant_nb_for_cols(cols)) {
-    case 1: quantize_rows_kernel<1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, codes, scales, gs); break;
-    case 2: quantize_rows_kernel<2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, codes, scales, gs); break;
-    case 4: quantize_rows_kernel<4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, codes, scales, gs); break;
-    case 8: quantize_rows_kernel<8><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, codes, scales, gs); break;
-    default: quantize_rows_kernel<0><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, codes, scales, gs); break;
+  const int64_t nbl = (cols / 16 + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(rows);
+  const int c = static_cast<int>(cols);
+  switch (nbl) {
+    case 1: quantize_rows_block_kernel<1><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 2: quantize_rows_block_kernel<2><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 3: quantize_rows_block_kernel<3><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 4: quantize_rows_block_kernel<4><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 5: quantize_rows_block_kernel<5><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 6: quantize_rows_block_kernel<6><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 7: quantize_rows_block_kernel<7><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    case 8: quantize_rows_block_kernel<8><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
+    default:
+      quantize_rows_long_kernel<<<static_cast<unsigned>((rows + 3) / 4), 256, 0, s>>>(x, rows, c, ld, codes,
+                                                                                     scales, gs);
+      break;
   }
   return hipGetLastError();
 }
