@@ -108,14 +108,14 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float* v) {
 // fp16 holds them exactly.  The converter applies only a power-of-two scale,
 // so the scale goes through a packed fp16 multiply instead.
 __device__ __forceinline__ half8 dequant8_f16(uint32_t codes, half2v scale2) {
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * scale2;
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * scale2;
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * scale2;
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * scale2;
-  half8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * scale2;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * scale2;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * scale2;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * scale2;
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  const half4 lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const half4 hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ half2v e4m3_half2(uint32_t b) {

@@ -66,7 +66,9 @@ __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&ac
       for (int i = 0; i < 4; ++i) {
         const float hg = acc[fh][fm][i] * alpha;
         const float hu = acc[FNH + fh][fm][i] * alpha;
-        a[i] = hg / (1.0f + __expf(-hg)) * hu;
+        // silu(hg) = hg / (1 + e^-hg) with the hardware exp and reciprocal
+        // (about 1 ulp each; e^-hg overflowing to inf gives silu = -0)
+        a[i] = hg * __builtin_amdgcn_rcpf(1.0f + __expf(-hg)) * hu;
         am = fmaxf(am, fabsf(a[i]));
       }
       if (m < nrows) {
@@ -445,12 +447,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel (many rows per expert: prefill).  64-row tiles; the token
-// operand is staged in LDS as fp16 in K chunks of 256; each wave streams the
-// records of one weight unit (4 fragments of 16 rows) per chunk.
+// Tiled kernel (many rows per expert: prefill).  One block = a tile of up to
+// 16*FM token rows x 4 weight units (4 waves, one unit of 64 weight rows
+// each); every wave multiplies its unit with all the tile's token rows, so a
+// weight fragment dequantized in registers feeds FM MFMAs.  The token operand
+// is the exact fp16 copy of the quantized rows, brought into LDS one 128-wide
+// K step ahead by direct global->LDS copies (no registers, no VALU) into two
+// alternating buffers: 16-byte piece c of tile row r sits at slot c ^ (r mod
+// 16) of the row's 256 bytes, so the 16 rows one fragment read touches fall
+// in distinct banks.  Two blocks share a CU (two waves per SIMD), which keeps
+// the matrix cores fed while the other block waits at its barrier.
+//
+// Ordering of the copies.  Vector loads complete in issue order.  In step s
+// the block issues the copies of step s + 1 right after its barrier and the
+// weight refill of step s + 2 after its MFMAs, so at the start of step s + 1
+// exactly one refill (kRefillOps instructions) was issued after that step's
+// copies: waiting until at most kRefillOps loads are outstanding covers the
+// copies and nothing newer.  Scheduling barriers keep the compiler from
+// moving loads across these points.
 // ---------------------------------------------------------------------------
-constexpr int kTiledKC = 256;
-constexpr int kTiledPitch = kTiledKC + 8;  // fp16 elements per LDS row (16-byte pad)
+constexpr int kTiledWaves = 4;
+constexpr int kTiledThreads = kTiledWaves * kWave;
+constexpr int kRefillOps = kUnitFrags + 1;  // vector memory instructions of load_unit_step
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+// Workgroup barrier for the LDS operand only.  A full __syncthreads also
+// waits for every outstanding global load (the global->LDS copies count as
+// such), which would drain the weight prefetch; here the caller has already
+// waited for the copies it needs, this wave's LDS reads are complete
+// (lgkmcnt 0), and the memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Rows of the token operand for local row m of a tile: GEMM1 reads the
 // per-token quantized activations of token perm[row] / k, GEMM2 the
@@ -473,91 +509,116 @@ __device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrow
   }
 }
 
+// The global->LDS copies of one K step of the tile's fp16 token rows (this
+// wave's share; see the kernel comment for the piece placement).
+template <int NCP>
+__device__ __forceinline__ void tiled_copy_step(const _Float16* a16, const int* coff, uint8_t* buf,
+                                                int s, int wave) {
+#pragma unroll
+  for (int u = 0; u < NCP; ++u) {
+    auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + kTiledWaves * u));
+    __builtin_amdgcn_global_load_lds(a16 + coff[u] + 128 * s, d, 16, 0, 0);
+  }
+}
+
+// One K step: wait for this step's copies, start the next step's, MFMAs on
+// the LDS operand `cur` and the weight record in `w`, then refill `w` with
+// the record two steps ahead.
+template <int FM, int NCP>
+__device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
+                                           uint8_t* nxt, UnitStep& w, const uint8_t* rec, const _Float16* a16,
+                                           const int* coff, bool has_unit, int wave, int lane) {
+  const int g = lane >> 4, r16 = lane & 15;
+  wait_vmcnt<kRefillOps>();  // this step's copies have landed (see the kernel comment)
+  lds_barrier();             // ... in every wave; the other buffer is free
+  tiled_copy_step<NCP>(a16, coff, nxt, min(s + 1, S - 1), wave);  // (the last step's copy is unused)
+  __builtin_amdgcn_sched_barrier(0);
+  if (has_unit) {
+    half2v wsc[kUnitFrags][2];
+#pragma unroll
+    for (int f = 0; f < kUnitFrags; ++f) {
+      const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1));
+      wsc[f][0] = e4m3_to_half2(w16);
+      wsc[f][1] = e4m3_to_half2(w16 >> 8);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half8 bq[FM];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        bq[fm] = *reinterpret_cast<const half8*>(cur + (fm * 16 + r16) * 256 + 16 * ((4 * g + q) ^ r16));
+      half8 aq[kUnitFrags];
+#pragma unroll
+      for (int f = 0; f < kUnitFrags; ++f) aq[f] = dequant8_f16(word_of(w.c[f], q), wsc[f][q >> 1]);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int f = 0; f < kUnitFrags; ++f)
+          acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bq[fm], acc[f][fm], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_unit_step(w, rec + static_cast<int64_t>(min(s + 2, S - 1)) * kRecBytes, lane);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int FM, int MODE>
-__global__ __launch_bounds__(256) void moe_tiled_kernel(FwdParams p) {
+__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moe_tiled_kernel(FwdParams p) {
   constexpr int MT = 16 * FM;
-  __shared__ _Float16 lds[MT][kTiledPitch];
+  constexpr int NCP = MT * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[MT * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[MT * 256];
   __shared__ int s_src[MT];
   __shared__ int s_slot[MT];
   __shared__ float s_ginv[MT];
-  __shared__ float s_amax[4][MT];
+  __shared__ float s_amax[kTiledWaves][MT];
   if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
   const int4 td = p.tiles[blockIdx.x];
   const int e = td.x, row0 = td.y, nrows = td.z;
   const int K = MODE == 0 ? p.H : p.I;
-  const uint8_t* a_codes = MODE == 0 ? p.xq_codes : p.a2_codes;
-  const uint8_t* a_scales = MODE == 0 ? p.xq_scales : p.a2_scales;
-  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, s_slot);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int g = lane >> 4, r16 = lane & 15;
   const int S = ksteps(K);
+  const _Float16* a16 = MODE == 0 ? p.xq16 : p.a2q16;
+  const int t = threadIdx.x;
+  const int wave = t / kWave, lane = t & (kWave - 1);
+  const int g = lane >> 4, r16 = lane & 15;
   const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
-  const int j = blockIdx.y * 4 + wave;
+  const int j = blockIdx.y * kTiledWaves + wave;
   const bool has_unit = j < upe;  // the last band of units may be partial
   const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
                        (static_cast<int64_t>(e) * upe + (has_unit ? j : 0)) * S * kRecBytes;
+
+  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, s_slot);
+  __syncthreads();
+  // this wave's copies: instruction u covers tile rows 4 (wave + 4 u) .. + 3;
+  // lane l brings piece (l % 16) ^ (r % 16) of row r = 4 (wave + 4 u) + l / 16
+  int coff[NCP];
+#pragma unroll
+  for (int u = 0; u < NCP; ++u) {
+    const int r = 4 * (wave + kTiledWaves * u) + (lane >> 4);
+    const int pc = (lane & 15) ^ (r & 15);
+    coff[u] = max(s_src[r], 0) * K + 8 * pc;  // rows past nrows read row 0 (never stored)
+  }
+  tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);
+  UnitStep wb[2];
+  load_unit_step(wb[0], rec, lane);
+  load_unit_step(wb[1], rec + static_cast<int64_t>(min(1, S - 1)) * kRecBytes, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
   f32x4 acc[kUnitFrags][FM];
 #pragma unroll
   for (int f = 0; f < kUnitFrags; ++f)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < K; kc += kTiledKC) {
-    const int nsteps = min(kTiledKC, K - kc) / 128;
-    const int s0 = kc / 128;
-    UnitStep wb[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) load_unit_step(wb[d], rec + static_cast<int64_t>(min(s0 + d, S - 1)) * kRecBytes, lane);
-    __syncthreads();  // previous chunk consumed; row table ready
-    const int items = MT * nsteps * 4;
-    for (int it = threadIdx.x; it < items; it += 256) {
-      const int m = it / (nsteps * 4);
-      const int kk = (it - m * nsteps * 4) * 32;
-      const int src = s_src[m];
-      half8* dst = reinterpret_cast<half8*>(&lds[m][kk]);
-      if (src >= 0) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(a_codes + static_cast<int64_t>(src) * (K / 2) + (kc + kk) / 2);
-        const uint32_t sw = *reinterpret_cast<const uint16_t*>(a_scales + static_cast<int64_t>(src) * (K / 16) + (kc + kk) / 16);
-        const half2v s0h = e4m3_to_half2(sw), s1h = e4m3_to_half2(sw >> 8);
-        dst[0] = dequant8_f16(cw.x, s0h);
-        dst[1] = dequant8_f16(cw.y, s0h);
-        dst[2] = dequant8_f16(cw.z, s1h);
-        dst[3] = dequant8_f16(cw.w, s1h);
-      } else {
-        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        dst[0] = z; dst[1] = z; dst[2] = z; dst[3] = z;
-      }
-    }
-    __syncthreads();
-    if (has_unit) {
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (d < nsteps) {
-          half2v wsc[kUnitFrags][2];
-#pragma unroll
-          for (int f = 0; f < kUnitFrags; ++f) {
-            const uint32_t w16 = (f < 2 ? wb[d].sc.x : wb[d].sc.y) >> (16 * (f & 1));
-            wsc[f][0] = e4m3_to_half2(w16);
-            wsc[f][1] = e4m3_to_half2(w16 >> 8);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            half8 bq[FM];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-              bq[fm] = *reinterpret_cast<const half8*>(&lds[fm * 16 + r16][d * 128 + 32 * g + 8 * q]);
-#pragma unroll
-            for (int f = 0; f < kUnitFrags; ++f) {
-              const half8 aq = dequant8_f16(word_of(wb[d].c[f], q), wsc[f][q >> 1]);
-#pragma unroll
-              for (int fm = 0; fm < FM; ++fm)
-                acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[fm], acc[f][fm], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
+  // straight-line pairs of steps (buffer and register slot fixed per half),
+  // so that every wait above counts the same loads on every path
+  int s = 0;
+  for (; s + 1 < S; s += 2) {
+    tiled_step<FM, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FM, NCP>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
   }
+  if (s < S) tiled_step<FM, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
 
   float ginv[FM];
   int slots[FM];
@@ -583,7 +644,7 @@ __global__ __launch_bounds__(256) void moe_tiled_kernel(FwdParams p) {
 // Re-quantization of every expanded row for the tiled path: one wave per row
 // reads its act row (I binary32 values), takes the row amax over the GEMM1
 // band partials, and quantizes 16-element blocks (lane b handles blocks b,
-// b + 64, ...).
+// b + 64, ...); it also writes the dequantized fp16 copy GEMM2 reads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -599,13 +660,18 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
     const uint32_t sb = requant_block(p.act + row * I + 16 * b, g2, lo, hi);
     *reinterpret_cast<uint2*>(p.a2_codes + row * (I / 2) + 8 * b) = make_uint2(lo, hi);
     p.a2_scales[row * (I / 16) + b] = static_cast<uint8_t>(sb);
+    if (p.a2q16) {
+      const half2v sc = e4m3_to_half2(sb);
+      half8* d = reinterpret_cast<half8*>(p.a2q16 + row * I + 16 * b);
+      d[0] = dequant8_f16(lo, sc);
+      d[1] = dequant8_f16(hi, sc);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-constexpr int kTiledFM = 4;
 
 int stream_lds_bytes(int fm, int K) { return 16 * fm * ((K / 2 + 16) + (K / 16 + 4)); }
 
@@ -640,7 +706,8 @@ void choose_gemm(int64_t T, FwdParams* p) {
     p->mt = 32;
     p->gemm_kind = kGemmStream;
   } else {
-    p->mt = 16 * kTiledFM;
+    // prefill: 128-row tiles once experts average that many rows, else 64
+    p->mt = avg >= 128 ? 128 : 64;
     p->gemm_kind = kGemmTiled;
   }
   if (p->gemm_kind == kGemmStream) {
@@ -650,7 +717,7 @@ void choose_gemm(int64_t T, FwdParams* p) {
     p->g1_bands = (I / 32) / (4 / p->g1_ks);
   } else {
     p->g1_ks = p->g2_ks = 1;
-    p->g1_bands = (I / 32 + 3) / 4;
+    p->g1_bands = (I / 32 + kTiledWaves - 1) / kTiledWaves;
   }
 }
 
@@ -688,12 +755,22 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     else
       launch_stream_fm<2>(p, max_tiles, s, ev);
   } else {
-    const int nb1 = (p.I / 32 + 3) / 4;
-    moe_tiled_kernel<kTiledFM, 0><<<dim3(max_tiles, nb1), 256, 0, s>>>(p);
-    if (ev) (void)hipEventRecord(ev[2], s);
-    moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-    const int nb2 = (p.H / 64 + 3) / 4;
-    moe_tiled_kernel<kTiledFM, 1><<<dim3(max_tiles, nb2), 256, 0, s>>>(p);
+    const int nb1 = (p.I / 32 + kTiledWaves - 1) / kTiledWaves;
+    const int nb2 = (p.H / 64 + kTiledWaves - 1) / kTiledWaves;
+    // a multiple of 8 tiles keeps every band of a tile on the same XCD (its
+    // token rows are then fetched into one L2)
+    const int gx = (max_tiles + 7) / 8 * 8;
+    if (p.mt == 128) {
+      moe_tiled_kernel<8, 0><<<dim3(gx, nb1), kTiledThreads, 0, s>>>(p);
+      if (ev) (void)hipEventRecord(ev[2], s);
+      moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
+      moe_tiled_kernel<8, 1><<<dim3(gx, nb2), kTiledThreads, 0, s>>>(p);
+    } else {
+      moe_tiled_kernel<4, 0><<<dim3(gx, nb1), kTiledThreads, 0, s>>>(p);
+      if (ev) (void)hipEventRecord(ev[2], s);
+      moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
+      moe_tiled_kernel<4, 1><<<dim3(gx, nb2), kTiledThreads, 0, s>>>(p);
+    }
     if (ev) (void)hipEventRecord(ev[3], s);
   }
   return hipGetLastError();

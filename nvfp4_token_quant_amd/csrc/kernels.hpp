@@ -48,7 +48,9 @@ __host__ __device__ constexpr int64_t packed_bytes(int64_t units, int K) {
 //           the tile is staged once in LDS as FP4 codes + scales; each wave
 //           streams the records of one unit (or a K range of it) with a
 //           register prefetch.
-//   tiled:  64-row tiles; token operand staged in K chunks as fp16.
+//   tiled:  64- or 128-row tiles; the token operand is read as fp16 (the
+//           exact dequantized copy the prologue / re-quantization write) and
+//           staged in LDS one K step at a time.
 enum GemmKind { kGemmStream = 0, kGemmTiled = 1 };
 
 struct FwdParams {
@@ -66,6 +68,7 @@ struct FwdParams {
   uint8_t* xq_codes;
   uint8_t* xq_scales;
   float* xq_g;
+  _Float16* xq16;  // [T, H] the same values dequantized (code x block scale, exact in fp16); tiled path only
   // routing and expandInputRows
   int32_t* topk_ids;
   float* topk_w;
@@ -84,6 +87,7 @@ struct FwdParams {
   uint8_t* a2_codes;
   uint8_t* a2_scales;
   float* a2_g;
+  _Float16* a2q16;  // [R, I] dequantized re-quantized act (exact in fp16); tiled path only
   float* y;        // [R, H] (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
   // weights: unit records (see kRecBytes) and per-expert global scales

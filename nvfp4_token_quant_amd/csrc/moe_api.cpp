@@ -61,6 +61,8 @@ struct moe_workspace {
   uint8_t* xq_codes;
   uint8_t* xq_scales;
   float* xq_g;
+  _Float16* xq16;  // fp16 copies of the quantized token operands (tiled path)
+  _Float16* a2q16;
   // routing / permutation
   int32_t* topk_ids;
   float* topk_w;
@@ -108,6 +110,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->xq_codes), T * H / 2);
   f(reinterpret_cast<void**>(&w->xq_scales), T * H / 16);
   f(reinterpret_cast<void**>(&w->xq_g), T * 4);
+  f(reinterpret_cast<void**>(&w->xq16), T * H * 2);
   f(reinterpret_cast<void**>(&w->topk_ids), R * 4);
   f(reinterpret_cast<void**>(&w->topk_w), R * 4);
   f(reinterpret_cast<void**>(&w->loc_rank), R * 4);
@@ -124,6 +127,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->a2_codes), R * I / 2);
   f(reinterpret_cast<void**>(&w->a2_scales), R * I / 16);
   f(reinterpret_cast<void**>(&w->a2_g), R * 4);
+  f(reinterpret_cast<void**>(&w->a2q16), R * I * 2);
   f(reinterpret_cast<void**>(&w->y), det ? R * H * 4 : 0);
   f(reinterpret_cast<void**>(&w->out_acc), det ? 0 : T * H * 4);
   f(reinterpret_cast<void**>(&w->w13), nvfp4::packed_bytes(nvfp4::w13_units(E, I), static_cast<int>(H)));
@@ -358,6 +362,9 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.xq_codes = ws->xq_codes;
   p.xq_scales = ws->xq_scales;
   p.xq_g = ws->xq_g;
+  // the fp16 copies are only written and read by the tiled (prefill) kernels
+  p.xq16 = p.gemm_kind == nvfp4::kGemmTiled ? ws->xq16 : nullptr;
+  p.a2q16 = p.gemm_kind == nvfp4::kGemmTiled ? ws->a2q16 : nullptr;
   p.topk_ids = ws->topk_ids;
   p.topk_w = ws->topk_w;
   p.loc_rank = ws->loc_rank;

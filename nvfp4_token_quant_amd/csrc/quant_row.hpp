@@ -49,10 +49,19 @@ __device__ __forceinline__ void load_row(RowRegs<NB>& rr, const uint16_t* __rest
 
 // Row amax -> g, then every block of the row; the block amaxes of the first
 // pass are reused by the second.
+// The dequantized values of one quantized block (code x block scale; exact
+// in fp16) as two 16-byte stores.
+__device__ __forceinline__ void store_block_f16(_Float16* dst, uint32_t lo, uint32_t hi, uint32_t sb) {
+  const half2v sc = e4m3_half2(sb);
+  half8* d = reinterpret_cast<half8*>(dst);
+  d[0] = dequant8_f16(lo, sc);
+  d[1] = dequant8_f16(hi, sc);
+}
+
 template <int NB>
 __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nblk, uint8_t* __restrict__ crow,
                                                   uint8_t* __restrict__ srow, float* __restrict__ gout,
-                                                  int lane) {
+                                                  int lane, _Float16* __restrict__ x16row = nullptr) {
   float bam[NB];
   float am = 0.0f;
 #pragma unroll
@@ -71,6 +80,7 @@ __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nbl
       const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
       *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
       srow[b] = static_cast<uint8_t>(sb);
+      if (x16row) store_block_f16(x16row + 16 * b, lo, hi, sb);
     }
   }
   if (lane == 0) *gout = g;
@@ -79,11 +89,11 @@ __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nbl
 template <int NB>
 __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
                                   uint8_t* __restrict__ crow, uint8_t* __restrict__ srow,
-                                  float* __restrict__ gout, int lane) {
+                                  float* __restrict__ gout, int lane, _Float16* __restrict__ x16row = nullptr) {
   if constexpr (NB > 0) {
     RowRegs<NB> rr;
     load_row<NB>(rr, xrow, nblk, lane);
-    quantize_row_regs<NB>(rr, nblk, crow, srow, gout, lane);
+    quantize_row_regs<NB>(rr, nblk, crow, srow, gout, lane, x16row);
   } else {
     // Rows too long for the register cache: amax pass, then quantize pass.
     float am = 0.0f;
@@ -100,6 +110,7 @@ __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
       const uint32_t sb = quantize_block16(f, g, lo, hi);
       *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
       srow[b] = static_cast<uint8_t>(sb);
+      if (x16row) store_block_f16(x16row + 16 * b, lo, hi, sb);
     }
     if (lane == 0) *gout = g;
   }
