@@ -87,12 +87,12 @@ __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&ac
 // column band; the re-quantization kernel reduces them).
 template <int MT>
 __device__ __forceinline__ void g1_store_band_amax(const FwdParams& p, float (*s_amax)[MT], int row0,
-                                                   int nrows) {
+                                                   int nrows, int band, int nbands) {
   __syncthreads();
   if (threadIdx.x < MT && static_cast<int>(threadIdx.x) < nrows) {
     const int m = threadIdx.x;
     const float v = fmaxf(fmaxf(s_amax[0][m], s_amax[1][m]), fmaxf(s_amax[2][m], s_amax[3][m]));
-    p.act_amax[static_cast<int64_t>(row0 + m) * gridDim.y + blockIdx.y] = v;
+    p.act_amax[static_cast<int64_t>(row0 + m) * nbands + band] = v;
   }
 }
 
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
     }
-    g1_store_band_amax<MT>(p, s_amax, row0, nrows);
+    g1_store_band_amax<MT>(p, s_amax, row0, nrows, blockIdx.y, gridDim.y);
   } else if (kp == 0) {
     g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
   }
@@ -512,19 +512,20 @@ __device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrow
 // The global->LDS copies of one K step of the tile's fp16 token rows (this
 // wave's share; see the kernel comment for the piece placement).
 template <int NCP>
-__device__ __forceinline__ void tiled_copy_step(const _Float16* a16, const int* coff, uint8_t* buf,
+__device__ __forceinline__ void tiled_copy_step(const _Float16* a16, const int* coff_lds, uint8_t* buf,
                                                 int s, int wave) {
+  // this lane's source offsets are kept in LDS to spare registers
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
     auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + kTiledWaves * u));
-    __builtin_amdgcn_global_load_lds(a16 + coff[u] + 128 * s, d, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a16 + coff_lds[u] + 128 * s, d, 16, 0, 0);
   }
 }
 
 // One K step: wait for this step's copies, start the next step's, MFMAs on
 // the LDS operand `cur` and the weight record in `w`, then refill `w` with
 // the record two steps ahead.
-template <int FM, int NCP>
+template <int FM, int NCP, bool kInterleave>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
                                            uint8_t* nxt, UnitStep& w, const uint8_t* rec, const _Float16* a16,
                                            const int* coff, bool has_unit, int wave, int lane) {
@@ -534,27 +535,42 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
   tiled_copy_step<NCP>(a16, coff, nxt, min(s + 1, S - 1), wave);  // (the last step's copy is unused)
   __builtin_amdgcn_sched_barrier(0);
   if (has_unit) {
-    half2v wsc[kUnitFrags][2];
+    // The step's 4*FM (q, fm) token fragments are read from LDS two ahead of
+    // their MFMAs (a rolling three-fragment window), so the read latency
+    // hides behind the previous fragments' MFMAs.
+    constexpr int NI = 4 * FM;
+    auto ldb = [&](int i) {
+      const int q = i / FM, fm = i % FM;
+      return *reinterpret_cast<const half8*>(cur + (fm * 16 + r16) * 256 + 16 * ((4 * g + q) ^ r16));
+    };
+    half8 bb[3];
+    bb[0] = ldb(0);
+    bb[1] = ldb(1);
+    half8 aq[kUnitFrags];
 #pragma unroll
-    for (int f = 0; f < kUnitFrags; ++f) {
-      const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1));
-      wsc[f][0] = e4m3_to_half2(w16);
-      wsc[f][1] = e4m3_to_half2(w16 >> 8);
+    for (int i = 0; i < NI; ++i) {
+      const int q = i / FM, fm = i % FM;
+      if (i + 2 < NI) bb[(i + 2) % 3] = ldb(i + 2);
+      if (fm == 0) {
+#pragma unroll
+        for (int f = 0; f < kUnitFrags; ++f) {
+          // scale of this q's 16-element block (q 0-1: first byte, q 2-3: second)
+          const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1) + 8 * (q >> 1));
+          aq[f] = dequant8_f16(word_of(w.c[f], q), e4m3_to_half2(w16));
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < kUnitFrags; ++f)
+        acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bb[i % 3], acc[f][fm], 0, 0, 0);
     }
+    // Pin the order for the scheduler: the two first reads, then per
+    // fragment one read two ahead and its four MFMAs (dequantization VALU
+    // is placed freely between them).
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      half8 bq[FM];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        bq[fm] = *reinterpret_cast<const half8*>(cur + (fm * 16 + r16) * 256 + 16 * ((4 * g + q) ^ r16));
-      half8 aq[kUnitFrags];
-#pragma unroll
-      for (int f = 0; f < kUnitFrags; ++f) aq[f] = dequant8_f16(word_of(w.c[f], q), wsc[f][q >> 1]);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int f = 0; f < kUnitFrags; ++f)
-          acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bq[fm], acc[f][fm], 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      if (i + 2 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -573,8 +589,16 @@ void moe_tiled_kernel(FwdParams p) {
   __shared__ int s_slot[MT];
   __shared__ float s_ginv[MT];
   __shared__ float s_amax[kTiledWaves][MT];
-  if (static_cast<int>(blockIdx.x) >= *p.n_tiles) return;
-  const int4 td = p.tiles[blockIdx.x];
+  __shared__ __attribute__((aligned(16))) int s_coff[kTiledThreads * NCP];
+  // XCD-aware order: consecutive blocks go to the 8 XCDs in turn, so block L
+  // runs on XCD L % 8 as that XCD's (L / 8)-th block; give each XCD whole
+  // tiles (tile % 8 == XCD) with all their bands in a row, so the bands of a
+  // tile follow each other on one L2 and share its token rows.
+  const int nb = gridDim.x / p.tiled_gx;  // bands per tile
+  const int L = blockIdx.x, slot = L >> 3;
+  const int band = slot % nb, tile = 8 * (slot / nb) + (L & 7);
+  if (tile >= *p.n_tiles) return;
+  const int4 td = p.tiles[tile];
   const int e = td.x, row0 = td.y, nrows = td.z;
   const int K = MODE == 0 ? p.H : p.I;
   const int S = ksteps(K);
@@ -583,7 +607,7 @@ void moe_tiled_kernel(FwdParams p) {
   const int wave = t / kWave, lane = t & (kWave - 1);
   const int g = lane >> 4, r16 = lane & 15;
   const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
-  const int j = blockIdx.y * kTiledWaves + wave;
+  const int j = band * kTiledWaves + wave;
   const bool has_unit = j < upe;  // the last band of units may be partial
   const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
                        (static_cast<int64_t>(e) * upe + (has_unit ? j : 0)) * S * kRecBytes;
@@ -592,14 +616,14 @@ void moe_tiled_kernel(FwdParams p) {
   __syncthreads();
   // this wave's copies: instruction u covers tile rows 4 (wave + 4 u) .. + 3;
   // lane l brings piece (l % 16) ^ (r % 16) of row r = 4 (wave + 4 u) + l / 16
-  int coff[NCP];
+  int* coff = s_coff + t * NCP;
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
     const int r = 4 * (wave + kTiledWaves * u) + (lane >> 4);
     const int pc = (lane & 15) ^ (r & 15);
     coff[u] = max(s_src[r], 0) * K + 8 * pc;  // rows past nrows read row 0 (never stored)
   }
-  tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);
+  tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);  // (reads back this thread's own writes)
   UnitStep wb[2];
   load_unit_step(wb[0], rec, lane);
   load_unit_step(wb[1], rec + static_cast<int64_t>(min(1, S - 1)) * kRecBytes, lane);
@@ -613,12 +637,15 @@ void moe_tiled_kernel(FwdParams p) {
 
   // straight-line pairs of steps (buffer and register slot fixed per half),
   // so that every wait above counts the same loads on every path
+  // the interleaved schedule needs more registers than GEMM1's (larger)
+  // epilogue leaves, so only GEMM2 uses it
+  constexpr bool kIl = MODE == 1;
   int s = 0;
   for (; s + 1 < S; s += 2) {
-    tiled_step<FM, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
-    tiled_step<FM, NCP>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FM, NCP, kIl>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FM, NCP, kIl>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
   }
-  if (s < S) tiled_step<FM, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+  if (s < S) tiled_step<FM, NCP, kIl>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
 
   float ginv[FM];
   int slots[FM];
@@ -634,7 +661,7 @@ void moe_tiled_kernel(FwdParams p) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
     }
-    g1_store_band_amax<MT>(p, s_amax, row0, nrows);
+    g1_store_band_amax<MT>(p, s_amax, row0, nrows, band, nb);
   } else if (has_unit) {
     g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
   }
@@ -759,17 +786,17 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     const int nb2 = (p.H / 64 + kTiledWaves - 1) / kTiledWaves;
     // a multiple of 8 tiles keeps every band of a tile on the same XCD (its
     // token rows are then fetched into one L2)
-    const int gx = (max_tiles + 7) / 8 * 8;
+    const int gx = (max_tiles + 7) / 8 * 8;  // == p.tiled_gx
     if (p.mt == 128) {
-      moe_tiled_kernel<8, 0><<<dim3(gx, nb1), kTiledThreads, 0, s>>>(p);
+      moe_tiled_kernel<8, 0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
       if (ev) (void)hipEventRecord(ev[2], s);
       moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-      moe_tiled_kernel<8, 1><<<dim3(gx, nb2), kTiledThreads, 0, s>>>(p);
+      moe_tiled_kernel<8, 1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
     } else {
-      moe_tiled_kernel<4, 0><<<dim3(gx, nb1), kTiledThreads, 0, s>>>(p);
+      moe_tiled_kernel<4, 0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
       if (ev) (void)hipEventRecord(ev[2], s);
       moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-      moe_tiled_kernel<4, 1><<<dim3(gx, nb2), kTiledThreads, 0, s>>>(p);
+      moe_tiled_kernel<4, 1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
     }
     if (ev) (void)hipEventRecord(ev[3], s);
   }

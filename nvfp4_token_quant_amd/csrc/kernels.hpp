@@ -59,6 +59,7 @@ struct FwdParams {
   int gemm_kind;      // GemmKind
   int g1_ks, g2_ks;   // stream kernels: waves sharing one unit's K range (1, 2, 4)
   int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
+  int tiled_gx;       // tiled kernels: tile slots of the grid (max tiles rounded up to 8)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
   // caller tensors
   const uint16_t* x;

@@ -389,6 +389,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.w2g = ws->w2g;
   p.dummy = ws->dummy;
   const int64_t max_tiles = tiles_bound(p.R, E, p.mt);
+  p.tiled_gx = static_cast<int>((max_tiles + 7) / 8 * 8);
   if (max_tiles > ws->max_tiles_cap) return fail(NVFP4_ERR_INVALID_ARG, "internal: tile bound exceeds capacity");
   hipError_t e = nvfp4::launch_moe_forward(p, static_cast<int>(max_tiles), static_cast<hipStream_t>(stream),
                                            ws->timing ? ws->events : nullptr);
