@@ -81,7 +81,6 @@ struct FwdParams {
   int32_t* inv;         // [R] t*k+j -> row
   int4* tiles;          // [max_tiles] (expert, row0, nrows, 0)
   int32_t* n_tiles;     // device scalar
-  uint32_t* ticket;     // device scalar, 0 between launches
   // intermediates
   float* act;       // [R, I]
   float* act_amax;  // [R, g1_bands <= I / 32] partial row amax per GEMM1 column band

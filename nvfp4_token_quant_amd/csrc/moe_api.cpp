@@ -74,7 +74,6 @@ struct moe_workspace {
   int32_t* inv;
   int4* tiles;
   int32_t* n_tiles;
-  uint32_t* ticket;
   // intermediates
   float* act;
   float* act_amax;
@@ -121,7 +120,6 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->inv), R * 4);
   f(reinterpret_cast<void**>(&w->tiles), w->max_tiles_cap * 16);
   f(reinterpret_cast<void**>(&w->n_tiles), 4);
-  f(reinterpret_cast<void**>(&w->ticket), 4);
   f(reinterpret_cast<void**>(&w->act), R * I * 4);
   f(reinterpret_cast<void**>(&w->act_amax), R * n_amax * 4);
   f(reinterpret_cast<void**>(&w->a2_codes), R * I / 2);
@@ -288,8 +286,7 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
     return status;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = nvfp4::launch_fill_u32(w->ticket, 1, 0u, s);
-  if (e == hipSuccess) e = nvfp4::launch_fill_u32(reinterpret_cast<uint32_t*>(w->dummy), nvfp4::kRecBytes / 4, 0u, s);
+  hipError_t e = nvfp4::launch_fill_u32(reinterpret_cast<uint32_t*>(w->dummy), nvfp4::kRecBytes / 4, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     free_all(w);
@@ -375,7 +372,6 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.inv = ws->inv;
   p.tiles = ws->tiles;
   p.n_tiles = ws->n_tiles;
-  p.ticket = ws->ticket;
   p.act = ws->act;
   p.act_amax = ws->act_amax;
   p.a2_codes = ws->a2_codes;

@@ -127,107 +127,23 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
 }
 
 // ---------------------------------------------------------------------------
-// Prologue.  Each block takes `tpb` consecutive tokens; each wave quantizes
-// and routes tokens of the block, then the block computes, for every (t, j),
-// its rank among equal experts inside the block and the block's per-expert
-// counts.  The last block to finish (ticket counter; no waiting) turns the
-// per-block counts into the stable expandInputRows permutation: rows of one
-// expert in ascending (t, j) order, the per-expert offsets and the M-tile list
-// of the grouped GEMMs.
+// Prologue for large batches, three kernels.
+//  1. route: each block takes `tpb` consecutive tokens; each wave quantizes
+//     and routes tokens of the block, then the block computes, for every
+//     (t, j), its rank among equal experts inside the block and the block's
+//     per-expert counts.
+//  2. schedule (one block): per expert, exclusive scan of the per-block
+//     counts down the blocks (experts x block chunks in parallel), then scans
+//     over experts for the row offsets and M-tile bases, and the tile list.
+//  3. place (one thread per (t, j)): row = offset[e] + block base[b][e] +
+//     rank, giving the stable expandInputRows permutation (rows of one
+//     expert in ascending (t, j) order) and its inverse.
 // ---------------------------------------------------------------------------
-__device__ void build_schedule_last_block(const FwdParams& p, int nblocks, int tpb) {
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts];
-  __shared__ int32_t s_tbase[kMaxExperts];
-  __shared__ int32_t s_part[256][2];
-  const int tid = threadIdx.x;
-  const int E = p.E;
-  // 1. per expert: exclusive scan of the per-block counts down the blocks
-  for (int e = tid; e < E; e += 256) {
-    int run = 0;
-    int b = 0;
-    for (; b + 8 <= nblocks; b += 8) {
-      int c[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = p.blk_counts[(b + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        p.blk_counts[(b + u) * E + e] = run;
-        run += c[u];
-      }
-    }
-    for (; b < nblocks; ++b) {
-      const int c = p.blk_counts[b * E + e];
-      p.blk_counts[b * E + e] = run;
-      run += c;
-    }
-    s_cnt[e] = run;
-    p.counts[e] = run;
-  }
-  __syncthreads();
-  // 2. exclusive scans over experts: row offsets and tile bases
-  const int per = (E + 255) / 256;
-  int rsum = 0, tsum = 0;
-  for (int u = 0; u < per; ++u) {
-    const int e = tid * per + u;
-    if (e < E) {
-      rsum += s_cnt[e];
-      tsum += (s_cnt[e] + p.mt - 1) / p.mt;
-    }
-  }
-  s_part[tid][0] = rsum;
-  s_part[tid][1] = tsum;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int a0 = 0, a1 = 0;
-    if (tid >= o) {
-      a0 = s_part[tid - o][0];
-      a1 = s_part[tid - o][1];
-    }
-    __syncthreads();
-    s_part[tid][0] += a0;
-    s_part[tid][1] += a1;
-    __syncthreads();
-  }
-  int rbase = s_part[tid][0] - rsum, tbase = s_part[tid][1] - tsum;
-  for (int u = 0; u < per; ++u) {
-    const int e = tid * per + u;
-    if (e < E) {
-      s_off[e] = rbase;
-      s_tbase[e] = tbase;
-      p.offsets[e] = rbase;
-      rbase += s_cnt[e];
-      tbase += (s_cnt[e] + p.mt - 1) / p.mt;
-    }
-  }
-  if (tid == 255) {
-    p.offsets[E] = s_part[255][0];
-    *p.n_tiles = s_part[255][1];
-  }
-  __syncthreads();
-  // 3. M-tiles: (expert, first row, rows)
-  for (int e = tid; e < E; e += 256) {
-    const int c = s_cnt[e];
-    const int nt = (c + p.mt - 1) / p.mt;
-    for (int i = 0; i < nt; ++i)
-      p.tiles[s_tbase[e] + i] = make_int4(e, s_off[e] + i * p.mt, min(p.mt, c - i * p.mt), 0);
-  }
-  // 4. placement
-  for (int i = tid; i < p.R; i += 256) {
-    const int t = i / p.k;
-    const int b = t / tpb;
-    const int e = p.topk_ids[i];
-    const int row = s_off[e] + p.blk_counts[b * E + e] + p.loc_rank[i];
-    p.perm[row] = i;
-    p.inv[i] = row;
-  }
-  if (tid == 0) *p.ticket = 0u;
-}
+constexpr int kSchedThreads = 1024;
 
 template <int NB, int KPL>
 __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   __shared__ int32_t s_ids[kMaxTokensPerRouteBlock * kMaxTopK];
-  __shared__ int s_last;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int t0 = blockIdx.x * tpb;
   const int ntok = min(tpb, p.T - t0);
@@ -256,13 +172,107 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
     for (int j = 0; j < nent; ++j) c += (s_ids[j] == e);
     p.blk_counts[blockIdx.x * p.E + e] = c;
   }
-  __threadfence();
+}
+
+__global__ __launch_bounds__(kSchedThreads) void moe_schedule_kernel(FwdParams p, int nblocks) {
+  __shared__ int32_t s_part[kSchedThreads];  // [chunk][expert] partial sums, then bases
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts];
+  __shared__ int32_t s_tbase[kMaxExperts];
+  __shared__ int32_t s_scan[kSchedThreads][2];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  // 1. blocks are cut into `chunks` chunks; thread (chunk c, expert e) sums
+  //    its chunk, a scan over the chunks gives each chunk's base, and the
+  //    thread writes the exclusive per-block bases of its chunk
+  const int chunks = max(1, kSchedThreads / E);
+  const int cs = (nblocks + chunks - 1) / chunks;
+  const int e1 = tid % E, c1 = tid / E;
+  const bool act = c1 < chunks;
+  const int b0 = min(c1 * cs, nblocks), b1 = min(b0 + cs, nblocks);
+  if (act) {
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += p.blk_counts[b * E + e1];
+    s_part[c1 * E + e1] = sum;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(p.ticket, 1u) == gridDim.x - 1) ? 1 : 0;
+  if (tid < E) {
+    int run = 0;
+    for (int c = 0; c < chunks; ++c) {
+      const int v = s_part[c * E + tid];
+      s_part[c * E + tid] = run;
+      run += v;
+    }
+    s_cnt[tid] = run;
+    p.counts[tid] = run;
+  }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  build_schedule_last_block(p, gridDim.x, tpb);
+  if (act) {
+    int run = s_part[c1 * E + e1];
+    for (int b = b0; b < b1; ++b) {
+      const int v = p.blk_counts[b * E + e1];
+      p.blk_counts[b * E + e1] = run;
+      run += v;
+    }
+  }
+  // 2. exclusive scans over experts: row offsets and tile bases
+  const int per = (E + kSchedThreads - 1) / kSchedThreads;
+  int rsum = 0, tsum = 0;
+  for (int u = 0; u < per; ++u) {
+    const int e = tid * per + u;
+    if (e < E) {
+      rsum += s_cnt[e];
+      tsum += (s_cnt[e] + p.mt - 1) / p.mt;
+    }
+  }
+  s_scan[tid][0] = rsum;
+  s_scan[tid][1] = tsum;
+  __syncthreads();
+  for (int o = 1; o < kSchedThreads; o <<= 1) {
+    int a0 = 0, a1 = 0;
+    if (tid >= o) {
+      a0 = s_scan[tid - o][0];
+      a1 = s_scan[tid - o][1];
+    }
+    __syncthreads();
+    s_scan[tid][0] += a0;
+    s_scan[tid][1] += a1;
+    __syncthreads();
+  }
+  int rbase = s_scan[tid][0] - rsum, tbase = s_scan[tid][1] - tsum;
+  for (int u = 0; u < per; ++u) {
+    const int e = tid * per + u;
+    if (e < E) {
+      s_off[e] = rbase;
+      s_tbase[e] = tbase;
+      p.offsets[e] = rbase;
+      rbase += s_cnt[e];
+      tbase += (s_cnt[e] + p.mt - 1) / p.mt;
+    }
+  }
+  if (tid == kSchedThreads - 1) {
+    p.offsets[E] = s_scan[kSchedThreads - 1][0];
+    *p.n_tiles = s_scan[kSchedThreads - 1][1];
+  }
+  __syncthreads();
+  // 3. M-tiles: (expert, first row, rows)
+  for (int e = tid; e < E; e += kSchedThreads) {
+    const int c = s_cnt[e];
+    const int nt = (c + p.mt - 1) / p.mt;
+    for (int i = 0; i < nt; ++i)
+      p.tiles[s_tbase[e] + i] = make_int4(e, s_off[e] + i * p.mt, min(p.mt, c - i * p.mt), 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.R) return;
+  const int t = i / p.k;
+  const int b = t / tpb;
+  const int e = p.topk_ids[i];
+  const int row = p.offsets[e] + p.blk_counts[b * p.E + e] + p.loc_rank[i];
+  p.perm[row] = i;
+  p.inv[i] = row;
 }
 
 // ---------------------------------------------------------------------------
@@ -552,6 +562,8 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
     moe_route_kernel<NB, 4><<<nblocks, 256, 0, s>>>(p, tpb);
   else
     moe_route_kernel<NB, kMaxExperts / kWave><<<nblocks, 256, 0, s>>>(p, tpb);
+  moe_schedule_kernel<<<1, kSchedThreads, 0, s>>>(p, nblocks);
+  moe_place_kernel<<<(p.R + 255) / 256, 256, 0, s>>>(p, tpb);
 }
 
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
