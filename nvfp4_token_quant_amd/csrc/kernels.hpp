@@ -9,10 +9,10 @@ namespace nvfp4 {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
-constexpr int kMaxRouteBlocks = 256;       // prologue blocks for T <= 32768
+constexpr int kMaxRouteBlocks = 1024;      // prologue blocks for T <= 131072
 constexpr int kMaxTokensPerRouteBlock = 128;
 
-// Tokens per prologue block: one token per wave up to 1024 tokens, then as
+// Tokens per prologue block: one token per wave up to 4096 tokens, then as
 // many as keep the block count at kMaxRouteBlocks.
 inline int route_tokens_per_block(int64_t T) {
   if (T <= 4 * kMaxRouteBlocks) return 4;

@@ -132,14 +132,14 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
 //     and routes tokens of the block, then the block computes, for every
 //     (t, j), its rank among equal experts inside the block and the block's
 //     per-expert counts.
-//  2. schedule (one block): per expert, exclusive scan of the per-block
-//     counts down the blocks (experts x block chunks in parallel), then scans
-//     over experts for the row offsets and M-tile bases, and the tile list.
-//  3. place (one thread per (t, j)): row = offset[e] + block base[b][e] +
-//     rank, giving the stable expandInputRows permutation (rows of one
-//     expert in ascending (t, j) order) and its inverse.
+//  2. schedule: per expert, exclusive scan of the per-block counts down the
+//     blocks, and the expert's total.
+//  3. place (one thread per (t, j)): scans over experts for the row offsets
+//     (and, in block 0, the M-tile list), then row = offset[e] + block
+//     base[b][e] + rank, giving the stable expandInputRows permutation (rows
+//     of one expert in ascending (t, j) order) and its inverse.
 // ---------------------------------------------------------------------------
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 256;
 
 template <int NB, int KPL>
 __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
@@ -174,103 +174,122 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   }
 }
 
+// 2. One block per kSchedExperts experts, kSchedThreads / kSchedExperts
+//    threads per expert; each thread owns a chunk of consecutive route blocks:
+//    chunk sums -> inclusive scan over the chunks in LDS -> each thread writes
+//    the exclusive per-block bases of its chunk; the expert's total goes to
+//    counts[e].
+constexpr int kSchedExperts = 2;
+constexpr int kSchedPerExpert = kSchedThreads / kSchedExperts;
+
 __global__ __launch_bounds__(kSchedThreads) void moe_schedule_kernel(FwdParams p, int nblocks) {
-  __shared__ int32_t s_part[kSchedThreads];  // [chunk][expert] partial sums, then bases
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts];
-  __shared__ int32_t s_tbase[kMaxExperts];
-  __shared__ int32_t s_scan[kSchedThreads][2];
-  const int tid = threadIdx.x;
+  __shared__ int32_t s_sum[kSchedExperts][kSchedPerExpert];
   const int E = p.E;
-  // 1. blocks are cut into `chunks` chunks; thread (chunk c, expert e) sums
-  //    its chunk, a scan over the chunks gives each chunk's base, and the
-  //    thread writes the exclusive per-block bases of its chunk
-  const int chunks = max(1, kSchedThreads / E);
-  const int cs = (nblocks + chunks - 1) / chunks;
-  const int e1 = tid % E, c1 = tid / E;
-  const bool act = c1 < chunks;
-  const int b0 = min(c1 * cs, nblocks), b1 = min(b0 + cs, nblocks);
-  if (act) {
-    int sum = 0;
-    for (int b = b0; b < b1; ++b) sum += p.blk_counts[b * E + e1];
-    s_part[c1 * E + e1] = sum;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int c = 0; c < chunks; ++c) {
-      const int v = s_part[c * E + tid];
-      s_part[c * E + tid] = run;
-      run += v;
-    }
-    s_cnt[tid] = run;
-    p.counts[tid] = run;
-  }
-  __syncthreads();
-  if (act) {
-    int run = s_part[c1 * E + e1];
-    for (int b = b0; b < b1; ++b) {
-      const int v = p.blk_counts[b * E + e1];
-      p.blk_counts[b * E + e1] = run;
-      run += v;
+  const int le = threadIdx.x / kSchedPerExpert, c = threadIdx.x % kSchedPerExpert;
+  const int e = blockIdx.x * kSchedExperts + le;
+  const bool valid = e < E;
+  const int cs = (nblocks + kSchedPerExpert - 1) / kSchedPerExpert;
+  const int b0 = min(c * cs, nblocks), b1 = min(b0 + cs, nblocks);
+  constexpr int kU = 16;  // loads in batches of 16, all in flight together
+  int sum = 0;
+  if (valid) {
+    for (int b = b0; b < b1; b += kU) {
+      int v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = p.blk_counts[min(b + u, b1 - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) sum += b + u < b1 ? v[u] : 0;
     }
   }
-  // 2. exclusive scans over experts: row offsets and tile bases
-  const int per = (E + kSchedThreads - 1) / kSchedThreads;
+  // inclusive scan over the expert's chunks (Hillis-Steele in LDS)
+  s_sum[le][c] = sum;
+  __syncthreads();
+  for (int o = 1; o < kSchedPerExpert; o <<= 1) {
+    const int a = c >= o ? s_sum[le][c - o] : 0;
+    __syncthreads();
+    s_sum[le][c] += a;
+    __syncthreads();
+  }
+  if (!valid) return;
+  if (c == kSchedPerExpert - 1) p.counts[e] = s_sum[le][c];
+  int run = s_sum[le][c] - sum;
+  for (int b = b0; b < b1; b += kU) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = p.blk_counts[min(b + u, b1 - 1) * E + e];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (b + u < b1) {
+        p.blk_counts[(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+  }
+}
+
+// 3. Every block scans the per-expert totals in LDS for the row offsets (E is
+//    at most kMaxExperts), then places its entries; block 0 also publishes the
+//    offsets, the tile count and the M-tile list.
+__global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
+  __shared__ int32_t s_off[kMaxExperts];
+  __shared__ int32_t s_tb[kMaxExperts];
+  __shared__ int32_t s_part[256][2];
+  const int tid = threadIdx.x;
+  const int E = p.E, mt = p.mt;
+  const int per = (E + 255) / 256;
   int rsum = 0, tsum = 0;
   for (int u = 0; u < per; ++u) {
     const int e = tid * per + u;
     if (e < E) {
-      rsum += s_cnt[e];
-      tsum += (s_cnt[e] + p.mt - 1) / p.mt;
+      const int cnt = p.counts[e];
+      rsum += cnt;
+      tsum += (cnt + mt - 1) / mt;
     }
   }
-  s_scan[tid][0] = rsum;
-  s_scan[tid][1] = tsum;
+  s_part[tid][0] = rsum;
+  s_part[tid][1] = tsum;
   __syncthreads();
-  for (int o = 1; o < kSchedThreads; o <<= 1) {
+  for (int o = 1; o < 256; o <<= 1) {
     int a0 = 0, a1 = 0;
     if (tid >= o) {
-      a0 = s_scan[tid - o][0];
-      a1 = s_scan[tid - o][1];
+      a0 = s_part[tid - o][0];
+      a1 = s_part[tid - o][1];
     }
     __syncthreads();
-    s_scan[tid][0] += a0;
-    s_scan[tid][1] += a1;
+    s_part[tid][0] += a0;
+    s_part[tid][1] += a1;
     __syncthreads();
   }
-  int rbase = s_scan[tid][0] - rsum, tbase = s_scan[tid][1] - tsum;
+  int rb = s_part[tid][0] - rsum, tb = s_part[tid][1] - tsum;
   for (int u = 0; u < per; ++u) {
     const int e = tid * per + u;
     if (e < E) {
-      s_off[e] = rbase;
-      s_tbase[e] = tbase;
-      p.offsets[e] = rbase;
-      rbase += s_cnt[e];
-      tbase += (s_cnt[e] + p.mt - 1) / p.mt;
+      const int cnt = p.counts[e];
+      s_off[e] = rb;
+      s_tb[e] = tb;
+      rb += cnt;
+      tb += (cnt + mt - 1) / mt;
     }
   }
-  if (tid == kSchedThreads - 1) {
-    p.offsets[E] = s_scan[kSchedThreads - 1][0];
-    *p.n_tiles = s_scan[kSchedThreads - 1][1];
-  }
   __syncthreads();
-  // 3. M-tiles: (expert, first row, rows)
-  for (int e = tid; e < E; e += kSchedThreads) {
-    const int c = s_cnt[e];
-    const int nt = (c + p.mt - 1) / p.mt;
-    for (int i = 0; i < nt; ++i)
-      p.tiles[s_tbase[e] + i] = make_int4(e, s_off[e] + i * p.mt, min(p.mt, c - i * p.mt), 0);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += 256) {
+      p.offsets[e] = s_off[e];
+      const int cnt = p.counts[e];
+      const int nt = (cnt + mt - 1) / mt;
+      for (int i = 0; i < nt; ++i) p.tiles[s_tb[e] + i] = make_int4(e, s_off[e] + i * mt, min(mt, cnt - i * mt), 0);
+    }
+    if (tid == 255) {
+      p.offsets[E] = s_part[255][0];
+      *p.n_tiles = s_part[255][1];
+    }
   }
-}
-
-__global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.x * 256 + tid;
   if (i >= p.R) return;
   const int t = i / p.k;
   const int b = t / tpb;
   const int e = p.topk_ids[i];
-  const int row = p.offsets[e] + p.blk_counts[b * p.E + e] + p.loc_rank[i];
+  const int row = s_off[e] + p.blk_counts[b * E + e] + p.loc_rank[i];
   p.perm[row] = i;
   p.inv[i] = row;
 }
@@ -562,7 +581,7 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
     moe_route_kernel<NB, 4><<<nblocks, 256, 0, s>>>(p, tpb);
   else
     moe_route_kernel<NB, kMaxExperts / kWave><<<nblocks, 256, 0, s>>>(p, tpb);
-  moe_schedule_kernel<<<1, kSchedThreads, 0, s>>>(p, nblocks);
+  moe_schedule_kernel<<<(p.E + kSchedExperts - 1) / kSchedExperts, kSchedThreads, 0, s>>>(p, nblocks);
   moe_place_kernel<<<(p.R + 255) / 256, 256, 0, s>>>(p, tpb);
 }
 
