@@ -31,6 +31,36 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP/C++ sources of the library (names and contents)."""
+    import hashlib
+
+    d = hashlib.sha256()
+    src = os.path.join(ROOT, "nvfp4_token_quant_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        d.update(name.encode())
+        with open(os.path.join(src, name), "rb") as f:
+            d.update(f.read())
+    return d.hexdigest()
+
+
+def measured_traffic(workload, T, stage):
+    """HBM bytes per launch of one stage, from the profiler's FETCH_SIZE and
+    WRITE_SIZE counters scaled by a plain copy of known size, as recorded in
+    profiles/hbm_traffic.json; None when no record exists for this workload
+    or the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    e = rec.get("stages", {}).get(f"{workload}|T={T}|{stage}")
+    return None if e is None else e["fetch_bytes"] + e["write_bytes"]
 
 
 def parse():
@@ -197,15 +227,17 @@ def main():
     tokens_per_s = T * args.steps / (t1 - t0)
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
+    workload = f"nvfp4_moe_layer_{L.name}"
+    traffic = measured_traffic(workload, T, dominant)
     mfma_bound = layer_flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > layer_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         achieved = stage_flops[dominant] / (mean_ms[dominant] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": dominant}
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic, "kernel": dominant}
     else:
         achieved = stage_bytes[dominant] / (mean_ms[dominant] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dominant}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant}
     layer_time_s = ms_per_step * 1e-3
     layer_roof = {
         "bytes": layer_bytes, "flops": layer_flops,
@@ -233,7 +265,7 @@ def main():
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1 + e4m3 block-16 + f32 global) operands, f16 MFMA, f32 accumulate",
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
-        "config": {"workload": f"nvfp4_moe_layer_{L.name}", "layer_id": args.layer, "T": T, "H": H,
+        "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
                    "weights_rotated": args.rotate, "hip_graph": not args.eager,
                    "parallelism": "none (1 GPU)"},
@@ -311,7 +343,9 @@ def bench_quantize(args):
         "config": {"workload": "nvfp4_quantize_per_token", "layer_id": 4, "T": T, "H": H,
                    "inputs_rotated": nrot, "hip_graph": False, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "quantize_rows",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("nvfp4_quantize_per_token", T, "quantize_rows"),
+                     "kernel": "quantize_rows",
                      "kernel_ms": kernel_ms, "bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }
