@@ -140,13 +140,17 @@ typedef struct moe_workspace moe_workspace;
  * "Implementation breakdown" items 1-3: sizing from the first forward's batch
  * crashed later, larger batches; the ceiling comes from configuration).
  * moe_token_ceiling() computes that ceiling from serving limits.
+ * Limits: 1 <= max_num_tokens <= 2^24, max_num_tokens * top_k <= 2^30 and
+ * max_num_tokens * hidden < 2^30 (the prefill kernels address one token
+ * operand of fp16 rows with 32-bit byte offsets); otherwise
+ * NVFP4_ERR_INVALID_ARG.
  * Synchronizes the device (allocation).  *out receives the handle.
  */
 int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** out);
 
 /*
  * Bind expert weights.  Codes, block scales and global scales are COPIED
- * into library-owned buffers in the kernels' fragment-major layout (the
+ * into library-owned buffers in the kernels' unit-record layout (the
  * *_blockscale_mma analogue of [P1] "Implementation breakdown" item 3; one
  * wave load then reads 1 KB of contiguous memory).  The caller's code
  * addresses are remembered: a later refresh_scales_inplace re-reads the

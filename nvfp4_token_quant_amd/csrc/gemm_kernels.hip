@@ -510,15 +510,26 @@ __device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrow
 }
 
 // The global->LDS copies of one K step of the tile's fp16 token rows (this
-// wave's share; see the kernel comment for the piece placement).
+// wave's share; see the kernel comment for the piece placement).  They are
+// buffer loads with the LDS bit: unlike global_load_lds (a FLAT instruction
+// that the compiler treats as touching both global memory and LDS), they
+// leave the LDS counter in order, so each wait for a token fragment waits
+// for that fragment's read only, not for every read issued after it.  The
+// resource's size also bounds every copy: a read past it returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tiled_rsrc(const _Float16* base, int64_t elems) {
+  // dword 3 = 0x00020000: 32-bit data format, no swizzle (raw buffer)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(base), static_cast<short>(0),
+                                           static_cast<int>(2 * elems), 0x00020000);
+}
+
 template <int NCP>
-__device__ __forceinline__ void tiled_copy_step(const _Float16* a16, const int* coff_lds, uint8_t* buf,
+__device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const int* coff_lds, uint8_t* buf,
                                                 int s, int wave) {
-  // this lane's source offsets are kept in LDS to spare registers
+  // this lane's source byte offsets are kept in LDS to spare registers
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
     auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + kTiledWaves * u));
-    __builtin_amdgcn_global_load_lds(a16 + coff_lds[u] + 128 * s, d, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, coff_lds[u] + 256 * s, 0, 0, 0);
   }
 }
 
@@ -527,7 +538,7 @@ __device__ __forceinline__ void tiled_copy_step(const _Float16* a16, const int* 
 // the record two steps ahead.
 template <int FM, int NCP, bool kInterleave>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
-                                           uint8_t* nxt, UnitStep& w, const uint8_t* rec, const _Float16* a16,
+                                           uint8_t* nxt, UnitStep& w, const uint8_t* rec, __amdgpu_buffer_rsrc_t a16,
                                            const int* coff, bool has_unit, int wave, int lane) {
   const int g = lane >> 4, r16 = lane & 15;
   wait_vmcnt<kRefillOps>();  // this step's copies have landed (see the kernel comment)
@@ -602,7 +613,11 @@ void moe_tiled_kernel(FwdParams p) {
   const int e = td.x, row0 = td.y, nrows = td.z;
   const int K = MODE == 0 ? p.H : p.I;
   const int S = ksteps(K);
-  const _Float16* a16 = MODE == 0 ? p.xq16 : p.a2q16;
+  // token operand: GEMM1 gathers rows of xq16 [T, K]; GEMM2 reads the tile's
+  // own rows of a2q16 [R, K] (offsets relative to the tile's first row)
+  const __amdgpu_buffer_rsrc_t a16 =
+      MODE == 0 ? tiled_rsrc(p.xq16, static_cast<int64_t>(p.T) * K)
+                : tiled_rsrc(p.a2q16 + static_cast<int64_t>(row0) * K, static_cast<int64_t>(nrows) * K);
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = t & (kWave - 1);
   const int g = lane >> 4, r16 = lane & 15;
@@ -621,7 +636,9 @@ void moe_tiled_kernel(FwdParams p) {
   for (int u = 0; u < NCP; ++u) {
     const int r = 4 * (wave + kTiledWaves * u) + (lane >> 4);
     const int pc = (lane & 15) ^ (r & 15);
-    coff[u] = max(s_src[r], 0) * K + 8 * pc;  // rows past nrows read row 0 (never stored)
+    // byte offset; rows past nrows read the first row (never stored)
+    const int src = MODE == 0 ? max(s_src[r], 0) : (r < nrows ? r : 0);
+    coff[u] = 2 * (src * K + 8 * pc);
   }
   tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);  // (reads back this thread's own writes)
   UnitStep wb[2];

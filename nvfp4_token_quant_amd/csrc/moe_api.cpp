@@ -257,6 +257,9 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
     return fail(NVFP4_ERR_INVALID_ARG, "unknown flags 0x%x", c.flags);
   if (c.max_num_tokens * c.top_k > (int64_t(1) << 30))
     return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * top_k too large");
+  if (c.max_num_tokens * c.hidden >= (int64_t(1) << 30))
+    return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * hidden must be < 2^30 (got %lld)",
+                (long long)(c.max_num_tokens * c.hidden));
   moe_workspace* w = new (std::nothrow) moe_workspace();
   if (!w) return fail(NVFP4_ERR_OOM, "host allocation failed");
   std::memset(static_cast<void*>(w), 0, sizeof(*w));
