@@ -49,10 +49,10 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 // for row m = 16 fm + r16; ginv[fm] = 1 / (that row's token global scale).
 // act = silu(h_gate) * h_up in fp32, stored with the row's amax over these
 // columns in s_amax[wave][m].
-template <int FM, int FNH>
+template <int FM, int FNH, int SM = 16 * FM>
 __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&acc)[2 * FNH][FM],
                                             int e, int row0, int nrows, int c0, const float (&ginv)[FM],
-                                            float (*s_amax)[16 * FM], int wave, int g, int r16) {
+                                            float (*s_amax)[SM], int wave, int g, int r16) {
   const float wginv = 1.0f / p.w13g[e];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
@@ -453,10 +453,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 // weight fragment dequantized in registers feeds FM MFMAs.  The token operand
 // is the exact fp16 copy of the quantized rows, brought into LDS one 128-wide
 // K step ahead by direct global->LDS copies (no registers, no VALU) into two
-// alternating buffers: 16-byte piece c of tile row r sits at slot c ^ (r mod
-// 16) of the row's 256 bytes, so the 16 rows one fragment read touches fall
-// in distinct banks.  Two blocks share a CU (two waves per SIMD), which keeps
-// the matrix cores fed while the other block waits at its barrier.
+// alternating buffers.  Layout of a buffer: 1 KB chunk (fm, g) (fm = 16-row
+// group of the tile, g = 64-byte quarter of the step's 256-byte row segment)
+// holds, at 256 q + 16 r, the 16 bytes (k = 32 g + 8 q .. + 7) of tile row
+// 16 fm + r.  One copy instruction fills one chunk (16 rows x 64 contiguous
+// bytes each); one MFMA operand read (fm, q) takes 256 contiguous bytes from
+// each of the four chunks (fm, g): on gfx950 that reads at the full LDS rate
+// of 256 B/clk, whereas 16 lanes reading 16 different 256-byte-strided rows
+// (even XOR-swizzled) take twice as long.  Two blocks share a CU (two waves
+// per SIMD), which keeps the matrix cores fed while the other block waits at
+// its barrier.
 //
 // Ordering of the copies.  Vector loads complete in issue order.  In step s
 // the block issues the copies of step s + 1 right after its barrier and the
@@ -468,6 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 // ---------------------------------------------------------------------------
 constexpr int kTiledWaves = 4;
 constexpr int kTiledThreads = kTiledWaves * kWave;
+constexpr int kTiledRows = 128;  // rows of a tile (8 groups of 16)
 constexpr int kRefillOps = kUnitFrags + 1;  // vector memory instructions of load_unit_step
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
@@ -536,7 +543,7 @@ __device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const
 // One K step: wait for this step's copies, start the next step's, MFMAs on
 // the LDS operand `cur` and the weight record in `w`, then refill `w` with
 // the record two steps ahead.
-template <int FM, int NCP, bool kInterleave>
+template <int FM, int NCP>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
                                            uint8_t* nxt, UnitStep& w, const uint8_t* rec, __amdgpu_buffer_rsrc_t a16,
                                            const int* coff, bool has_unit, int wave, int lane) {
@@ -552,7 +559,7 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
     constexpr int NI = 4 * FM;
     auto ldb = [&](int i) {
       const int q = i / FM, fm = i % FM;
-      return *reinterpret_cast<const half8*>(cur + (fm * 16 + r16) * 256 + 16 * ((4 * g + q) ^ r16));
+      return *reinterpret_cast<const half8*>(cur + 1024 * (4 * fm + g) + 256 * q + 16 * r16);
     };
     half8 bb[3];
     bb[0] = ldb(0);
@@ -589,28 +596,26 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FM, int MODE>
-__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void moe_tiled_kernel(FwdParams p) {
-  constexpr int MT = 16 * FM;
-  constexpr int NCP = MT * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[MT * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[MT * 256];
-  __shared__ int s_src[MT];
-  __shared__ int s_slot[MT];
-  __shared__ float s_ginv[MT];
-  __shared__ float s_amax[kTiledWaves][MT];
-  __shared__ __attribute__((aligned(16))) int s_coff[kTiledThreads * NCP];
-  // XCD-aware order: consecutive blocks go to the 8 XCDs in turn, so block L
-  // runs on XCD L % 8 as that XCD's (L / 8)-th block; give each XCD whole
-  // tiles (tile % 8 == XCD) with all their bands in a row, so the bands of a
-  // tile follow each other on one L2 and share its token rows.
-  const int nb = gridDim.x / p.tiled_gx;  // bands per tile
-  const int L = blockIdx.x, slot = L >> 3;
-  const int band = slot % nb, tile = 8 * (slot / nb) + (L & 7);
-  if (tile >= *p.n_tiles) return;
-  const int4 td = p.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
+// Shared memory of one tiled block (sized for the largest tile).
+struct TiledShared {
+  uint8_t lds[2][kTiledRows * 256] __attribute__((aligned(16)));
+  int src[kTiledRows];
+  int slot[kTiledRows];
+  float ginv[kTiledRows];
+  float amax[kTiledWaves][kTiledRows];
+  // per thread: the source offsets of its copy instructions (at most 8)
+  int coff[kTiledThreads * (kTiledRows * 16 / kWave / kTiledWaves)] __attribute__((aligned(16)));
+};
+static_assert(sizeof(TiledShared) <= 80 * 1024, "two tiled blocks must share a CU's LDS");
+
+// One tile whose rows fit in FMV 16-row groups: the copies, MFMAs and
+// epilogue cover only those groups, so a tile of few rows costs in
+// proportion to its rows (up to the next power of two of groups).
+template <int FMV, int MODE>
+__device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, int e, int row0, int nrows,
+                                           int band, int nb) {
+  constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
+  static_assert(kTiledThreads * NCP <= sizeof(TiledShared::coff) / sizeof(int), "copy offset table");
   const int K = MODE == 0 ? p.H : p.I;
   const int S = ksteps(K);
   // token operand: GEMM1 gathers rows of xq16 [T, K]; GEMM2 reads the tile's
@@ -626,19 +631,20 @@ void moe_tiled_kernel(FwdParams p) {
   const bool has_unit = j < upe;  // the last band of units may be partial
   const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
                        (static_cast<int64_t>(e) * upe + (has_unit ? j : 0)) * S * kRecBytes;
+  uint8_t* lds0 = sh.lds[0];
+  uint8_t* lds1 = sh.lds[1];
 
-  tile_rows<MODE>(p, row0, nrows, MT, s_src, s_ginv, s_slot);
-  __syncthreads();
-  // this wave's copies: instruction u covers tile rows 4 (wave + 4 u) .. + 3;
-  // lane l brings piece (l % 16) ^ (r % 16) of row r = 4 (wave + 4 u) + l / 16
-  int* coff = s_coff + t * NCP;
+  // this wave's copies: instruction u fills chunk c = wave + 4 u, i.e.
+  // (fm, g) = (c / 4, c % 4); lane l brings bytes 64 g + 16 (l / 16) .. + 15
+  // of the step's segment of tile row 16 fm + l % 16
+  int* coff = sh.coff + t * NCP;
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
-    const int r = 4 * (wave + kTiledWaves * u) + (lane >> 4);
-    const int pc = (lane & 15) ^ (r & 15);
+    const int c = wave + kTiledWaves * u;
+    const int r = 16 * (c >> 2) + (lane & 15);
     // byte offset; rows past nrows read the first row (never stored)
-    const int src = MODE == 0 ? max(s_src[r], 0) : (r < nrows ? r : 0);
-    coff[u] = 2 * (src * K + 8 * pc);
+    const int src = MODE == 0 ? max(sh.src[r], 0) : (r < nrows ? r : 0);
+    coff[u] = 2 * src * K + 64 * (c & 3) + 16 * (lane >> 4);
   }
   tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);  // (reads back this thread's own writes)
   UnitStep wb[2];
@@ -646,42 +652,72 @@ void moe_tiled_kernel(FwdParams p) {
   load_unit_step(wb[1], rec + static_cast<int64_t>(min(1, S - 1)) * kRecBytes, lane);
   __builtin_amdgcn_sched_barrier(0);
 
-  f32x4 acc[kUnitFrags][FM];
+  f32x4 acc[kUnitFrags][FMV];
 #pragma unroll
   for (int f = 0; f < kUnitFrags; ++f)
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int fm = 0; fm < FMV; ++fm) acc[f][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // straight-line pairs of steps (buffer and register slot fixed per half),
   // so that every wait above counts the same loads on every path
-  // the interleaved schedule needs more registers than GEMM1's (larger)
-  // epilogue leaves, so only GEMM2 uses it
-  constexpr bool kIl = MODE == 1;
   int s = 0;
   for (; s + 1 < S; s += 2) {
-    tiled_step<FM, NCP, kIl>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
-    tiled_step<FM, NCP, kIl>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
   }
-  if (s < S) tiled_step<FM, NCP, kIl>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+  if (s < S) tiled_step<FMV, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
 
-  float ginv[FM];
-  int slots[FM];
+  float ginv[FMV];
+  int slots[FMV];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    ginv[fm] = s_ginv[fm * 16 + r16];
-    slots[fm] = s_slot[fm * 16 + r16];
+  for (int fm = 0; fm < FMV; ++fm) {
+    ginv[fm] = sh.ginv[fm * 16 + r16];
+    slots[fm] = sh.slot[fm * 16 + r16];
   }
   if (MODE == 0) {
     if (has_unit) {
-      g1_epilogue<FM, 2>(p, acc, e, row0, nrows, 32 * j, ginv, s_amax, wave, g, r16);
+      g1_epilogue<FMV, 2, kTiledRows>(p, acc, e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16);
     } else if (g == 0) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
+      for (int fm = 0; fm < FMV; ++fm) sh.amax[wave][fm * 16 + r16] = 0.0f;
     }
-    g1_store_band_amax<MT>(p, s_amax, row0, nrows, band, nb);
+    g1_store_band_amax<kTiledRows>(p, sh.amax, row0, nrows, band, nb);
   } else if (has_unit) {
-    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
+    g2_epilogue<FMV, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moe_tiled_kernel(FwdParams p) {
+  __shared__ TiledShared sh;
+  // XCD-aware order: consecutive blocks go to the 8 XCDs in turn, so block L
+  // runs on XCD L % 8 as that XCD's (L / 8)-th block.  XCD x takes the x-th
+  // eighth of the tile list (tiles are sorted by expert), each tile with all
+  // its bands in a row: the bands of a tile share its token rows in that
+  // XCD's L2, and the tiles of one expert, running side by side, share its
+  // weight records there.
+  const int nb = gridDim.x / p.tiled_gx;  // bands per tile
+  const int L = blockIdx.x, slot = L >> 3;
+  const int ntiles = *p.n_tiles;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int band = slot % nb, local = slot / nb;
+  const int tile = (L & 7) * per_xcd + local;
+  if (local >= per_xcd || tile >= ntiles) return;
+  const int4 td = p.tiles[tile];
+  const int e = td.x, row0 = td.y, nrows = td.z;
+
+  tile_rows<MODE>(p, row0, nrows, kTiledRows, sh.src, sh.ginv, sh.slot);
+  __syncthreads();
+  const int groups = (nrows + 15) >> 4;
+  if (groups > 4)
+    tiled_tile<8, MODE>(p, sh, e, row0, nrows, band, nb);
+  else if (groups > 2)
+    tiled_tile<4, MODE>(p, sh, e, row0, nrows, band, nb);
+  else if (groups > 1)
+    tiled_tile<2, MODE>(p, sh, e, row0, nrows, band, nb);
+  else
+    tiled_tile<1, MODE>(p, sh, e, row0, nrows, band, nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -750,8 +786,9 @@ void choose_gemm(int64_t T, FwdParams* p) {
     p->mt = 32;
     p->gemm_kind = kGemmStream;
   } else {
-    // prefill: 128-row tiles once experts average that many rows, else 64
-    p->mt = avg >= 128 ? 128 : 64;
+    // prefill: 128-row tiles; a tile of fewer rows computes only the 16-row
+    // groups it needs
+    p->mt = kTiledRows;
     p->gemm_kind = kGemmTiled;
   }
   if (p->gemm_kind == kGemmStream) {
@@ -804,17 +841,10 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     // a multiple of 8 tiles keeps every band of a tile on the same XCD (its
     // token rows are then fetched into one L2)
     const int gx = (max_tiles + 7) / 8 * 8;  // == p.tiled_gx
-    if (p.mt == 128) {
-      moe_tiled_kernel<8, 0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
-      if (ev) (void)hipEventRecord(ev[2], s);
-      moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-      moe_tiled_kernel<8, 1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
-    } else {
-      moe_tiled_kernel<4, 0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
-      if (ev) (void)hipEventRecord(ev[2], s);
-      moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
-      moe_tiled_kernel<4, 1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
-    }
+    moe_tiled_kernel<0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
+    if (ev) (void)hipEventRecord(ev[2], s);
+    moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
+    moe_tiled_kernel<1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
     if (ev) (void)hipEventRecord(ev[3], s);
   }
   return hipGetLastError();
