@@ -9,9 +9,10 @@ NVFP4 quantization of x bf16 [16384, 7168]; one step = one launch).  Prints
 one JSON line.
 
 Timing: `steps` forwards after `warmup` untimed ones, bracketed by
-synchronizations; wall time gives `value` (tokens/s).  By default each timed
-forward is replayed from its own captured HIP graph (as decode serving does;
-`--eager` launches the kernels directly), back to back.  Every timed forward
+synchronizations; wall time gives `value` (tokens/s).  By default the timed
+forwards are captured into one HIP graph and replayed once (a decode
+deployment replays one graph per model step holding every layer; `--eager`
+launches the kernels directly).  Every timed forward
 records HIP events around its four kernels on its own stream, which give
 each kernel's mean duration; the dominant kernel's algorithmic bytes (or
 FLOPs) over that duration is `roofline.achieved`.  Expert weights rotate over
@@ -176,32 +177,43 @@ def main():
     lib = binding.lib()
     lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
     if not args.eager:
-        # one captured graph per timed forward, each with its own stage events
-        # (recorded inside the graph, so every replay re-records them)
+        # The timed forwards are captured into one HIP graph (each forward with
+        # its own stage events, recorded by the graph on every replay), the
+        # warm-up forwards into another; a decode deployment likewise replays
+        # one graph per model step holding every layer.
         evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
-        graphs = []
+        warm_evs = [[hip.event() for _ in range(5)] for _ in range(max(args.warmup, 1))]
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            for i in range(args.steps):
-                ly = layers[i % len(layers)]
-                lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in evs[i]]))
-                # record the events once outside the graph (HIP reports no elapsed
-                # time for events that were only ever recorded by graph nodes)
-                ly.forward_into(x, logits, out)
+
+        def capture(ev_sets, first):
+            with torch.cuda.stream(cap):
+                for i, ev in enumerate(ev_sets):
+                    ly = layers[(first + i) % len(layers)]
+                    lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
+                    # record the events once outside the graph (HIP reports no
+                    # elapsed time for events only ever recorded by graph nodes)
+                    ly.forward_into(x, logits, out)
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
-                    ly.forward_into(x, logits, out)
-                graphs.append(g)
+                    for i, ev in enumerate(ev_sets):
+                        ly = layers[(first + i) % len(layers)]
+                        lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
+                        ly.forward_into(x, logits, out)
+            return g
+
+        warm_graph = capture(warm_evs, 0)
+        graph = capture(evs, 0)
         torch.cuda.synchronize()
-        for g in graphs[: min(len(graphs), args.warmup)]:
-            g.replay()
+        warm_graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for g in graphs:
-            g.replay()
+        graph.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        for ev in warm_evs:
+            for e in ev:
+                hip.destroy(e)
     else:
         evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
         arrs = [(ctypes.c_void_p * 5)(*[e.value for e in step]) for step in evs]
@@ -267,7 +279,8 @@ def main():
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
-                   "weights_rotated": args.rotate, "hip_graph": not args.eager,
+                   "weights_rotated": args.rotate,
+                   "hip_graph": "one graph holding the timed forwards" if not args.eager else "none (eager)",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer_roofline": layer_roof,

@@ -794,7 +794,9 @@ void choose_gemm(int64_t T, FwdParams* p) {
   if (p->gemm_kind == kGemmStream) {
     const int64_t tiles = (R + p->mt - 1) / p->mt > active ? (R + p->mt - 1) / p->mt : active;
     p->g1_ks = choose_ks(tiles * (I / 32), I / 32, ksteps(H));
-    p->g2_ks = choose_ks(tiles * (H / 64), H / 64, ksteps(I));
+    // GEMM2 re-quantizes its tile's rows in every block, so splitting K
+    // (more blocks per tile) costs more than the extra parallelism gains
+    p->g2_ks = (H / 64) % 4 == 0 ? 1 : (H / 64) % 2 == 0 ? 2 : 4;
     p->g1_bands = (I / 32) / (4 / p->g1_ks);
   } else {
     p->g1_ks = p->g2_ks = 1;
