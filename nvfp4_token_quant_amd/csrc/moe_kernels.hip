@@ -449,6 +449,160 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prologue for decode-sized batches (T <= 64, E <= 256): block 0 routes every
+// token (16 lanes per token, all tokens in one pass) and keeps, per expert,
+// the 64-bit mask of the tokens routed to it.  A row's place in the stable
+// expandInputRows order is then the expert's offset plus the popcount of the
+// mask below its token, and the counts come from the masks as well, so the
+// whole schedule takes three block barriers.  Blocks 1.. quantize four token
+// rows each, one row per 256 threads (thread t owns 16-element blocks t,
+// t + 256, ...; the row amax is one LDS exchange between four waves).
+// ---------------------------------------------------------------------------
+constexpr int kTinyMaxT = 64, kTinyMaxE = 256;
+
+template <int NBL, int KPL>
+__global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdParams p) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int H = p.H, k = p.k, E = p.E, T = p.T;
+  if (blockIdx.x > 0) {
+    __shared__ float s_am[kSmallWaves];
+    const int q = tid >> 8, qt = tid & 255;  // quarter of the block and thread within it
+    const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * 4 + q;
+    const int nblk = H / 16;
+    const uint16_t* xrow = p.x + min(t, static_cast<int64_t>(T - 1)) * H;
+    uint4 v[NBL][2];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const uint4* src = reinterpret_cast<const uint4*>(xrow + 16 * min(qt + 256 * i, nblk - 1));
+      v[i][0] = src[0];
+      v[i][1] = src[1];
+    }
+    float bam[NBL];
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      bam[i] = amax16_bf16(v[i][0], v[i][1]);
+      if (qt + 256 * i < nblk) am = fmaxf(am, bam[i]);
+    }
+    am = wave_max(am);
+    if (lane == 0) s_am[wave] = am;
+    __syncthreads();
+    if (t >= T) return;
+    const float* sq = s_am + 4 * q;
+    const float g = global_scale(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3])));
+    uint8_t* crow = p.xq_codes + t * (H / 2);
+    uint8_t* srow = p.xq_scales + t * (H / 16);
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int b = qt + 256 * i;
+      if (b < nblk) {
+        float f[16];
+        unpack16(v[i][0], v[i][1], f);
+        uint32_t lo, hi;
+        const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
+        *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
+        srow[b] = static_cast<uint8_t>(sb);
+        if (p.xq16) store_block_f16(p.xq16 + t * H + 16 * b, lo, hi, sb);
+      }
+    }
+    if (qt == 0) p.xq_g[t] = g;
+    if (!p.deterministic) {
+      float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+      for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  __shared__ uint64_t s_mask[kTinyMaxE];
+  __shared__ int32_t s_ids[kTinyMaxT * kMaxTopK];
+  __shared__ int32_t s_off[kTinyMaxE];
+  __shared__ int32_t s_wsum[2][4];
+  if (tid < kTinyMaxE) s_mask[tid] = 0ull;
+  __syncthreads();
+  // 1. top-k of every token: wave w, group g routes token 4 w + g (waves
+  // past the last token skip it)
+  if (4 * wave < T) {
+    const int grp = lane >> 4, gl = lane & 15;
+    const int tk = 4 * wave + grp;
+    int id;
+    float w;
+    route_token_group16<KPL>(p.logits + static_cast<int64_t>(min(tk, T - 1)) * E, E, k, gl, id, w);
+    if (tk < T && gl < k) {
+      p.topk_ids[tk * k + gl] = id;
+      p.topk_w[tk * k + gl] = w;
+      s_ids[tk * k + gl] = id;
+      atomicOr(reinterpret_cast<unsigned long long*>(&s_mask[id]), 1ull << tk);
+    }
+  }
+  __syncthreads();
+  // 2. rows and tiles per expert, exclusive scans over the experts (waves 0-3)
+  int cnt = 0, nt = 0, ic = 0, it = 0;
+  if (tid < kTinyMaxE) {
+    cnt = tid < E ? __popcll(s_mask[tid]) : 0;
+    nt = (cnt + p.mt - 1) / p.mt;
+    ic = cnt;
+    it = nt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int a = __shfl_up(ic, o, kWave), b = __shfl_up(it, o, kWave);
+      if (lane >= o) {
+        ic += a;
+        it += b;
+      }
+    }
+    if (lane == kWave - 1) {
+      s_wsum[0][wave] = ic;
+      s_wsum[1][wave] = it;
+    }
+  }
+  __syncthreads();
+  if (tid < kTinyMaxE) {
+    int rows_total = 0, tiles_total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      if (w2 < wave) {
+        ic += s_wsum[0][w2];
+        it += s_wsum[1][w2];
+      }
+      rows_total += s_wsum[0][w2];
+      tiles_total += s_wsum[1][w2];
+    }
+    const int off = ic - cnt, tb = it - nt;
+    s_off[tid] = off;
+    if (tid < E) {
+      p.counts[tid] = cnt;
+      p.offsets[tid] = off;
+      for (int i = 0; i < nt; ++i) p.tiles[tb + i] = make_int4(tid, off + i * p.mt, min(p.mt, cnt - i * p.mt), 0);
+    }
+    if (tid == 0) {
+      p.offsets[E] = rows_total;
+      *p.n_tiles = tiles_total;
+    }
+  }
+  __syncthreads();
+  // 3. placement: row = offset of the expert + tokens routed to it before t
+  if (tid < T * k) {
+    const int tok = tid / k, e = s_ids[tid];
+    const int row = s_off[e] + __popcll(s_mask[e] & ((1ull << tok) - 1ull));
+    p.perm[row] = tid;
+    p.inv[tid] = row;
+  }
+}
+
+bool use_tiny_prologue(const FwdParams& p) {
+  return p.T <= kTinyMaxT && p.E <= kTinyMaxE && p.H / 16 <= 256 * 8 && p.T * p.k <= kSmallThreads;
+}
+
+template <int NBL>
+static void launch_prologue_tiny(const FwdParams& p, hipStream_t s) {
+  const int blocks = 1 + (p.T + 3) / 4;
+  if (p.E <= 16) moe_prologue_tiny_kernel<NBL, 1><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 32) moe_prologue_tiny_kernel<NBL, 2><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 64) moe_prologue_tiny_kernel<NBL, 4><<<blocks, kSmallThreads, 0, s>>>(p);
+  else if (p.E <= 128) moe_prologue_tiny_kernel<NBL, 8><<<blocks, kSmallThreads, 0, s>>>(p);
+  else moe_prologue_tiny_kernel<NBL, 16><<<blocks, kSmallThreads, 0, s>>>(p);
+}
+
 bool use_small_prologue(const FwdParams& p) {
   return p.T <= kSmallMaxT && p.E <= kSmallMaxE && p.R <= kSmallMaxR;
 }
@@ -588,7 +742,13 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* ev) {
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (use_small_prologue(p)) {
+  if (use_tiny_prologue(p)) {
+    const int nbl = (p.H / 16 + 255) / 256;
+    if (nbl <= 1) launch_prologue_tiny<1>(p, s);
+    else if (nbl <= 2) launch_prologue_tiny<2>(p, s);
+    else if (nbl <= 4) launch_prologue_tiny<4>(p, s);
+    else launch_prologue_tiny<8>(p, s);
+  } else if (use_small_prologue(p)) {
     switch (quant_nb_for_cols(p.H)) {
       case 1: launch_prologue_small<1>(p, s); break;
       case 2: launch_prologue_small<2>(p, s); break;
