@@ -175,46 +175,61 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
 }
 
 // 2. One block per kSchedExperts experts, kSchedThreads / kSchedExperts
-//    threads per expert; each thread owns a chunk of consecutive route blocks:
-//    chunk sums -> inclusive scan over the chunks in LDS -> each thread writes
-//    the exclusive per-block bases of its chunk; the expert's total goes to
-//    counts[e].
+//    threads (two waves) per expert; each thread owns a chunk of consecutive
+//    route blocks: chunk sums -> inclusive scan over the chunks (a shuffle
+//    scan per wave, one LDS exchange between the two waves) -> each thread
+//    writes the exclusive per-block bases of its chunk; the expert's total
+//    goes to counts[e].  Chunks of up to kU blocks stay in registers between
+//    the two passes.
 constexpr int kSchedExperts = 2;
 constexpr int kSchedPerExpert = kSchedThreads / kSchedExperts;
+static_assert(kSchedPerExpert == 2 * kWave, "two waves per expert");
 
 __global__ __launch_bounds__(kSchedThreads) void moe_schedule_kernel(FwdParams p, int nblocks) {
-  __shared__ int32_t s_sum[kSchedExperts][kSchedPerExpert];
+  __shared__ int32_t s_wave[kSchedExperts];
   const int E = p.E;
   const int le = threadIdx.x / kSchedPerExpert, c = threadIdx.x % kSchedPerExpert;
+  const int lane = threadIdx.x & (kWave - 1);
   const int e = blockIdx.x * kSchedExperts + le;
   const bool valid = e < E;
   const int cs = (nblocks + kSchedPerExpert - 1) / kSchedPerExpert;
   const int b0 = min(c * cs, nblocks), b1 = min(b0 + cs, nblocks);
   constexpr int kU = 16;  // loads in batches of 16, all in flight together
+  int v[kU];
   int sum = 0;
   if (valid) {
     for (int b = b0; b < b1; b += kU) {
-      int v[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) v[u] = p.blk_counts[min(b + u, b1 - 1) * E + e];
 #pragma unroll
       for (int u = 0; u < kU; ++u) sum += b + u < b1 ? v[u] : 0;
     }
   }
-  // inclusive scan over the expert's chunks (Hillis-Steele in LDS)
-  s_sum[le][c] = sum;
-  __syncthreads();
-  for (int o = 1; o < kSchedPerExpert; o <<= 1) {
-    const int a = c >= o ? s_sum[le][c - o] : 0;
-    __syncthreads();
-    s_sum[le][c] += a;
-    __syncthreads();
+  // inclusive scan over the expert's chunks
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int a = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += a;
   }
+  const bool second = c >= kWave;
+  if (!second && lane == kWave - 1) s_wave[le] = inc;
+  __syncthreads();
+  if (second) inc += s_wave[le];
   if (!valid) return;
-  if (c == kSchedPerExpert - 1) p.counts[e] = s_sum[le][c];
-  int run = s_sum[le][c] - sum;
+  if (c == kSchedPerExpert - 1) p.counts[e] = inc;
+  int run = inc - sum;
+  if (cs <= kU) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (b0 + u < b1) {
+        p.blk_counts[(b0 + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    return;
+  }
   for (int b = b0; b < b1; b += kU) {
-    int v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) v[u] = p.blk_counts[min(b + u, b1 - 1) * E + e];
 #pragma unroll
