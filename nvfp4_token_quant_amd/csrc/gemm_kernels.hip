@@ -610,7 +610,8 @@ static_assert(sizeof(TiledShared) <= 80 * 1024, "two tiled blocks must share a C
 
 // One tile whose rows fit in FMV 16-row groups: the copies, MFMAs and
 // epilogue cover only those groups, so a tile of few rows costs in
-// proportion to its rows (up to the next power of two of groups).
+// proportion to its rows (FMV is the smallest of 1, 2, 3, 4, 6, 8 groups
+// that holds them).
 template <int FMV, int MODE>
 __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, int e, int row0, int nrows,
                                            int band, int nb) {
@@ -710,10 +711,14 @@ void moe_tiled_kernel(FwdParams p) {
   tile_rows<MODE>(p, row0, nrows, kTiledRows, sh.src, sh.ginv, sh.slot);
   __syncthreads();
   const int groups = (nrows + 15) >> 4;
-  if (groups > 4)
+  if (groups > 6)
     tiled_tile<8, MODE>(p, sh, e, row0, nrows, band, nb);
-  else if (groups > 2)
+  else if (groups > 4)
+    tiled_tile<6, MODE>(p, sh, e, row0, nrows, band, nb);
+  else if (groups > 3)
     tiled_tile<4, MODE>(p, sh, e, row0, nrows, band, nb);
+  else if (groups > 2)
+    tiled_tile<3, MODE>(p, sh, e, row0, nrows, band, nb);
   else if (groups > 1)
     tiled_tile<2, MODE>(p, sh, e, row0, nrows, band, nb);
   else
