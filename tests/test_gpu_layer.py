@@ -145,6 +145,42 @@ def test_layer5_large(T):
     layer.close()
 
 
+@pytest.mark.parametrize("T", [65, 200, 257, 301])
+def test_prologue_paths_ragged_batches(T):
+    """Decode shapes at batch sizes that take the small-batch prologue
+    (65, 200) and the three-kernel prologue with ragged per-block token
+    counts (257, 301): every integer output on every token, the layer on a
+    sample of tokens."""
+    L = synth.LAYERS[2]
+    print(f"layer 2 T={T}", flush=True)
+    x, logits = synth.activations(2, T), synth.router_logits(2, T)
+    layer = _layer(2, max_tokens=512)
+    out = _run(layer, x, logits)
+    ids, w, _ = _check_integer_path(layer, 2, x, logits, T)
+    _check_requant(layer, 2, T)
+    toks = np.array([0, 1, T // 2, T - 2, T - 1])
+    ref = _oracle_out(2, x, ids, w, toks)
+    check_layer_tolerance(bf16_tensor_to_f64(out)[toks], ref)
+    layer.close()
+
+
+@pytest.mark.parametrize("T,deterministic", [(160, True), (256, True), (256, False)])
+def test_tiled_gemms_small_batch_prologue(T, deterministic):
+    """The tiny layer at batch sizes whose experts average more than 32 rows
+    (tiled GEMMs) while the small-batch prologue builds the schedule, with
+    both finalize modes; the whole output against the oracle."""
+    L = synth.LAYERS[1]
+    print(f"layer 1 T={T} deterministic={deterministic}", flush=True)
+    x, logits = synth.activations(1, T), synth.router_logits(1, T)
+    layer = _layer(1, deterministic=deterministic, max_tokens=T)
+    out = _run(layer, x, logits)
+    ids, w, _ = _check_integer_path(layer, 1, x, logits, T)
+    _check_requant(layer, 1, T)
+    ref = _oracle_out(1, x, ids, w, np.arange(T))
+    check_layer_tolerance(bf16_tensor_to_f64(out), ref)
+    layer.close()
+
+
 def test_deterministic_reproducible_and_permutation_invariant():
     L = synth.LAYERS[2]
     x, logits = synth.activations(2), synth.router_logits(2)
