@@ -59,11 +59,12 @@ def _declare(L):
     L.orc_permute.restype = None
     L.orc_permute.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
     L.orc_moe_layer.restype = ctypes.c_int
+    _F = ctypes.c_float
     L.orc_moe_layer.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64,
-                                _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+                                _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _P, _P]
     L.orc_moe_layer_dense.restype = None
     L.orc_moe_layer_dense.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
-                                      _P, _P, _P, _P, _P, _P, _P]
+                                      _P, _P, _P, _P, _P, _P, _F, _F, _P]
     L.orc_philox4x64_10.restype = None
     L.orc_philox4x64_10.argtypes = [_P, _P, _P]
     L.orc_synth_scale.restype = ctypes.c_float
@@ -192,12 +193,15 @@ class QuantWeights:
         self.w2c, self.w2s, self.w2g = _c(w2c, np.uint8), _c(w2s, np.uint8), _c(w2g, np.float32)
 
 
-def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False):
+def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, static_scales=None):
     """Layer output (float64 [n_tok, H]) for the listed tokens.
 
     x_bf16: uint16 [T, H]; ids int32 [T, k]; w float64 [T, k] (from router()).
+    static_scales: None (per-row global scales) or (g_x, g_a), the static
+    global scales of x and of the GEMM2 input.
     With debug=True also returns a dict of per-slot intermediates.
     """
+    gx, ga = (0.0, 0.0) if static_scales is None else static_scales
     x_bf16 = _c(x_bf16, np.uint16)
     ids = _c(ids, np.int32)
     w = _c(w, np.float64)
@@ -212,7 +216,8 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False):
                    g2=np.empty((n, k), np.float32))
     rc = lib().orc_moe_layer(
         _p(x_bf16), _p(ids), _p(w), _p(tokens), n, H, I, k, _p(qw.experts), qw.experts.size,
-        _p(qw.w13c), _p(qw.w13s), _p(qw.w13g), _p(qw.w2c), _p(qw.w2s), _p(qw.w2g), _p(out),
+        _p(qw.w13c), _p(qw.w13s), _p(qw.w13g), _p(qw.w2c), _p(qw.w2s), _p(qw.w2g),
+        float(np.float32(gx)), float(np.float32(ga)), _p(out),
         _p(dbg["y"]) if debug else None, _p(dbg["act"]) if debug else None,
         _p(dbg["c2"]) if debug else None, _p(dbg["S2"]) if debug else None,
         _p(dbg["g2"]) if debug else None)
@@ -221,7 +226,7 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False):
     return (out, dbg) if debug else out
 
 
-def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g):
+def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g, static_scales=None):
     x_bf16 = _c(x_bf16, np.uint16)
     ids = _c(ids, np.int32)
     w = _c(w, np.float64)
@@ -229,8 +234,10 @@ def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g):
     args = [_c(a, np.uint8) if a.dtype == np.uint8 else _c(a, np.float32)
             for a in (w13c, w13s, w13g, w2c, w2s, w2g)]
     out = np.empty((T, H), np.float64)
+    gx, ga = (0.0, 0.0) if static_scales is None else static_scales
     lib().orc_moe_layer_dense(_p(x_bf16), _p(ids), _p(w), T, H, I, E, k,
-                              *[_p(a) for a in args], _p(out))
+                              *[_p(a) for a in args], float(np.float32(gx)), float(np.float32(ga)),
+                              _p(out))
     return out
 
 

@@ -312,6 +312,12 @@ ORC_API void orc_permute(const int32_t* ids, int64_t T, int64_t k, int64_t E, in
 //   a32  = (float) act                     (READING: act stays binary32)
 //   (c2, S2, g2) = Q(a32)                  (READING: dynamic re-quantization
 //                                           per expanded row)
+// With static activation scales (the per-tensor input-scale contract the
+// per-token scheme replaces, [P1] "Feature and motivation"; the static
+// fc2_input_scale of "Source snippets"), x is quantized with the given g_x
+// and a32 with the given g_a instead of 2688 / amax of the row; the block
+// recipe is unchanged, so out-of-range values saturate (E4M3 at 448, E2M1
+// at 6).
 //   y    = a^2 . W^2[e]^T                  (binary64, length H)
 // out[t] = sum_j w[t, j] * y_(t, j)        (binary64)
 //
@@ -343,7 +349,7 @@ double silu(double z) { return z / (1.0 + std::exp(-z)); }
 // returns the intermediates for the debug entry point.
 void expert_row(const LayerArgs& a, const double* W13, const double* W2, const double* xh,
                 double* h, float* a32, uint8_t* c2, uint8_t* S2, float* g2, double* ah,
-                double* y) {
+                double* y, float static_ga) {
   const int64_t H = a.H, I = a.I;
   for (int64_t n = 0; n < 2 * I; ++n) {
     double acc = 0.0;
@@ -351,7 +357,7 @@ void expert_row(const LayerArgs& a, const double* W13, const double* W2, const d
     h[n] = acc;
   }
   for (int64_t i = 0; i < I; ++i) a32[i] = static_cast<float>(silu(h[i]) * h[I + i]);
-  *g2 = orc_global_scale(a32, I);
+  *g2 = static_ga > 0.0f ? static_ga : orc_global_scale(a32, I);
   quantize_with_g(a32, I, *g2, c2, S2);
   dequant_rows(c2, S2, *g2, 1, I, ah);
   for (int64_t n = 0; n < H; ++n) {
@@ -370,6 +376,8 @@ void expert_row(const LayerArgs& a, const double* W13, const double* W2, const d
 //   w13c [n_experts, 2I, H/2], w13s [n_experts, 2I, H/16], w13g [n_experts]
 //   w2c  [n_experts, H, I/2],  w2s  [n_experts, H, I/16],  w2g  [n_experts]
 //   out      [n_tok, H] binary64
+//   static_gx, static_ga  > 0: static global scales of x and of the GEMM2
+//                         input; <= 0: per-row scales (the default)
 // Optional debug outputs (may be null), per listed token and slot:
 //   y_dbg [n_tok, k, H], act_dbg [n_tok, k, I] (binary32),
 //   c2_dbg [n_tok, k, I/2], S2_dbg [n_tok, k, I/16], g2_dbg [n_tok, k]
@@ -378,8 +386,9 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
                           const int64_t* tokens, int64_t n_tok, int64_t H, int64_t I, int64_t k,
                           const int32_t* experts, int64_t n_experts, const uint8_t* w13c,
                           const uint8_t* w13s, const float* w13g, const uint8_t* w2c,
-                          const uint8_t* w2s, const float* w2g, double* out, double* y_dbg,
-                          float* act_dbg, uint8_t* c2_dbg, uint8_t* S2_dbg, float* g2_dbg) {
+                          const uint8_t* w2s, const float* w2g, float static_gx, float static_ga,
+                          double* out, double* y_dbg, float* act_dbg, uint8_t* c2_dbg,
+                          uint8_t* S2_dbg, float* g2_dbg) {
   LayerArgs a{H, I, k, w13c, w13s, w2c, w2s, w13g, w2g};
   int32_t max_e = 0;
   for (int64_t i = 0; i < n_experts; ++i) max_e = std::max(max_e, experts[i]);
@@ -399,7 +408,7 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
     for (int64_t ti = 0; ti < n_tok; ++ti) {
       const uint16_t* xr = x_bf16 + tokens[ti] * H;
       for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(xr[kk]);
-      float g = orc_global_scale(xf.data(), H);
+      float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
       quantize_with_g(xf.data(), H, g, c.data(), s.data());
       dequant_rows(c.data(), s.data(), g, 1, H, xh.data() + ti * H);
     }
@@ -427,7 +436,7 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
         if (ids[tokens[ti] * k + j] != experts[ei]) continue;
         double* y = ybuf.data() + (ti * k + j) * H;
         expert_row(a, W13.data(), W2.data(), xh.data() + ti * H, h.data(), a32.data(), c2.data(),
-                   S2.data(), g2.data(), ah.data(), y);
+                   S2.data(), g2.data(), ah.data(), y, static_ga);
         int64_t slot = ti * k + j;
         if (act_dbg) std::memcpy(act_dbg + slot * I, a32.data(), I * sizeof(float));
         if (c2_dbg) std::memcpy(c2_dbg + slot * (I / 2), c2.data(), I / 2);
@@ -459,7 +468,7 @@ ORC_API void orc_moe_layer_dense(const uint16_t* x_bf16, const int32_t* ids, con
                                  int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  const uint8_t* w13c, const uint8_t* w13s, const float* w13g,
                                  const uint8_t* w2c, const uint8_t* w2s, const float* w2g,
-                                 double* out) {
+                                 float static_gx, float static_ga, double* out) {
   LayerArgs a{H, I, k, w13c, w13s, w2c, w2s, w13g, w2g};
   std::vector<double> W13(static_cast<size_t>(2 * I * H)), W2(static_cast<size_t>(H * I));
   std::vector<double> xh(H), h(2 * I), ah(I), y(H);
@@ -472,11 +481,11 @@ ORC_API void orc_moe_layer_dense(const uint16_t* x_bf16, const int32_t* ids, con
     dequant_rows(w2c + e * H * (I / 2), w2s + e * H * (I / 16), w2g[e], H, I, W2.data());
     for (int64_t t = 0; t < T; ++t) {
       for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(x_bf16[t * H + kk]);
-      float g = orc_global_scale(xf.data(), H);
+      float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
       quantize_with_g(xf.data(), H, g, c.data(), s.data());
       dequant_rows(c.data(), s.data(), g, 1, H, xh.data());
       expert_row(a, W13.data(), W2.data(), xh.data(), h.data(), a32.data(), c2.data(),
-                 S2.data(), g2.data(), ah.data(), y.data());
+                 S2.data(), g2.data(), ah.data(), y.data(), static_ga);
       double wt = 0.0;
       for (int64_t j = 0; j < k; ++j)
         if (ids[t * k + j] == e) wt = w[t * k + j];
