@@ -106,13 +106,22 @@ int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, in
  * k slot outputs are summed in slot order j = 0..k-1 (bit-reproducible). */
 #define MOE_DETERMINISTIC_FINALIZE 0x1u
 
+/* Static activation scales.  [P1] "Feature and motivation": the per-token
+ * global scale replaces a static per-tensor input scale; "Source snippets":
+ * the static fc2_input_scale of GEMM2's input.  With this flag the forward
+ * quantizes x with one given global scale g_x and the SwiGLU output with one
+ * given g_a (set by moe_workspace_set_act_scales) instead of 2688 / amax of
+ * each row; the block recipe is the same, so values beyond 6 * 448 / g
+ * saturate (E4M3 block scale 448, E2M1 code 6). */
+#define MOE_STATIC_ACT_SCALES 0x2u
+
 typedef struct moe_config {
   int64_t max_num_tokens; /* token ceiling: every buffer is sized from it once */
   int64_t hidden;         /* H: multiple of 128 */
   int64_t inter;          /* I: multiple of 128 */
   int32_t num_experts;    /* E: 1..1024 */
   int32_t top_k;          /* k: 1..min(16, E) */
-  uint32_t flags;         /* MOE_DETERMINISTIC_FINALIZE or 0 */
+  uint32_t flags;         /* MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES, or 0 */
 } moe_config;
 
 /* NVFP4 expert weights, device pointers.  w13 rows [0, I) are the gate
@@ -196,6 +205,19 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
  * Enqueued on `stream`, ordered with forwards on the same stream.
  */
 int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
+
+/*
+ * Static activation scales (workspaces created with MOE_STATIC_ACT_SCALES):
+ * copies scales_dev[0] = g_x (global scale of x) and scales_dev[1] = g_a
+ * (global scale of GEMM2's input), binary32 encode-direction scales
+ * (dequantized value = code * block scale / g), finite and > 0, from device
+ * memory INTO the workspace, so a captured forward keeps its addresses and
+ * uses the new values on its next replay.  Must be called before the first
+ * forward; a forward before it returns NVFP4_ERR_INVALID_ARG.  Enqueued on
+ * `stream`; the caller's buffer must stay valid until that work has run.
+ * NVFP4_ERR_INVALID_ARG for a workspace without the flag or NULL pointers.
+ */
+int moe_workspace_set_act_scales(moe_workspace* ws, const float* scales_dev, void* stream);
 
 /* Free library-owned memory (never the caller's codes).  NULL is a no-op.
  * Synchronizes the device. */

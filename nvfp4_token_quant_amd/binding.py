@@ -20,6 +20,7 @@ SYNTH_PATH = os.path.join(HERE, "libnvfp4synth.so")
 HEADERS = [os.path.join(ROOT, "include", "nvfp4_moe.h"), os.path.join(ROOT, "include", "nvfp4_synth.h")]
 
 MOE_DETERMINISTIC_FINALIZE = 0x1
+MOE_STATIC_ACT_SCALES = 0x2
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARG", 2: "NVFP4_ERR_TOO_MANY_TOKENS",
           3: "NVFP4_ERR_ALIAS", 4: "NVFP4_ERR_NO_WEIGHTS", 5: "NVFP4_ERR_METADATA_CHANGED",
@@ -80,6 +81,8 @@ def lib():
         L.moe_workspace_destroy.argtypes = [_P]
         L.moe_token_ceiling.restype = ctypes.c_int
         L.moe_token_ceiling.argtypes = [_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
+        L.moe_workspace_set_act_scales.restype = ctypes.c_int
+        L.moe_workspace_set_act_scales.argtypes = [_P, _P, _P]
         L.moe_workspace_buffer.restype = ctypes.c_int
         L.moe_workspace_buffer.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(_I64)]
         _lib = L
@@ -228,9 +231,10 @@ class MoeLayer:
     """Workspace + bound weights.  forward(x, logits) -> bf16 [T, H]."""
 
     def __init__(self, max_num_tokens, hidden, inter, num_experts, top_k, deterministic=True,
-                 stream=None):
-        self.cfg = MoeConfig(max_num_tokens, hidden, inter, num_experts, top_k,
-                             MOE_DETERMINISTIC_FINALIZE if deterministic else 0)
+                 stream=None, static_act_scales=False):
+        flags = (MOE_DETERMINISTIC_FINALIZE if deterministic else 0) | \
+            (MOE_STATIC_ACT_SCALES if static_act_scales else 0)
+        self.cfg = MoeConfig(max_num_tokens, hidden, inter, num_experts, top_k, flags)
         h = ctypes.c_void_p()
         _check(lib().moe_workspace_create(ctypes.byref(self.cfg), _stream(stream), ctypes.byref(h)))
         self.handle = h
@@ -244,6 +248,14 @@ class MoeLayer:
     def refresh_scales(self, weights: NvFp4Weights, with_codes=True, stream=None):
         d = weights.desc(with_codes)
         _check(lib().refresh_scales_inplace(self.handle, ctypes.byref(d), _stream(stream)))
+
+    def set_act_scales(self, scales, stream=None):
+        """Static global scales (g_x, g_a): float32 tensor of 2 on the device,
+        copied into the workspace (workspaces made with static_act_scales)."""
+        _require(scales, torch.float32, "scales")
+        if scales.numel() != 2 or not scales.is_contiguous():
+            raise ValueError("scales must be a contiguous float32 tensor of 2 values (g_x, g_a)")
+        _check(lib().moe_workspace_set_act_scales(self.handle, _ptr(scales), _stream(stream)))
 
     def forward_into(self, x, logits, out, T=None, stream=None):
         T = x.shape[0] if T is None else T

@@ -49,14 +49,16 @@ __device__ __forceinline__ float global_scale(float a) {
   return __builtin_isinf(g) ? 3.402823466e38f : g;
 }
 
-// E4M3 encode, round to nearest even, for 0 <= s < 464 (the block scales of
-// the recipe never exceed 448 * (1 + 2^-22): t = RN(amax_b * g) <= 2688 (1 +
-// 2^-24)^2 since amax_b <= amax_row).  gfx950's converter produces the OCP
-// E4M3 byte directly; on [0, 464) it rounds to nearest even with values in
-// [448, 464) going to 448 (0x7E), the same bytes as the software definition
-// (every fp32 value of the interval was compared on the device).
+// E4M3 encode, round to nearest even, saturating at 448 (0x7E), for s >= 0.
+// gfx950's converter produces the OCP E4M3 byte directly; on [0, 464) it
+// rounds to nearest even with values in [448, 464) going to 448, the same
+// bytes as the software definition (every fp32 value of the interval was
+// compared on the device).  Per-row global scales keep the block scales
+// below 448 * (1 + 2^-22) (t = RN(amax_b * g) <= 2688 (1 + 2^-24)^2 since
+// amax_b <= amax_row); a static global scale can push them anywhere up to
+// +inf, which the clamp to 448 saturates (448 encodes as 0x7E either way).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(s, 0.0f, 0, false)) & 0xFFu;
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false)) & 0xFFu;
 }
 
 // E4M3 bits -> binary32 value (exact; b <= 0x7E or its negative).
@@ -149,9 +151,13 @@ __device__ __forceinline__ uint32_t quantize_block16_amax(const float* x, float 
   const uint32_t sb = e4m3_encode(div6_rn(t));
   const float d = e4m3_value(sb);
   const float r = d > 0.0f ? div_e4m3_rn(g, d) : 0.0f;
+  // |x r| <= 6.375 with a per-row global scale; with a static one the
+  // product can be anything up to +-inf, so it is clamped to the E2M1 range
+  // first (the saturating encoder maps every |v| >= 5 to 6, so the clamp
+  // changes no code)
   float v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = x[i] * r;
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_fmed3f(x[i] * r, -6.0f, 6.0f);
   lo = e2m1_pack8(v);
   hi = e2m1_pack8(v + 8);
   return sb;

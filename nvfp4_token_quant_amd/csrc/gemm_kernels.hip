@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
         a = fmaxf(a, p.act_amax[static_cast<int64_t>(row0 + min(m, nrows - 1)) * nb + c]);
       a = wave_max(a);
       if (lane == 0 && m < nrows) {
-        const float g2 = global_scale(a);
+        const float g2 = p.static_g ? p.static_g[1] : global_scale(a);
         s_g2[m] = g2;
         if (blockIdx.y == 0) p.a2_g[row0 + m] = g2;
       }
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
   const int I = p.I;
   float a = 0.0f;
   for (int j = lane; j < p.g1_bands; j += kWave) a = fmaxf(a, p.act_amax[row * p.g1_bands + j]);
-  const float g2 = global_scale(wave_max(a));
+  const float g2 = p.static_g ? p.static_g[1] : global_scale(wave_max(a));
   if (lane == 0) p.a2_g[row] = g2;
   for (int b = lane; b < I / 16; b += kWave) {
     uint32_t lo, hi;

@@ -61,6 +61,7 @@ struct FwdParams {
   int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
   int tiled_gx;       // tiled kernels: tile slots of the grid (max tiles rounded up to 8)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
+  const float* static_g;  // NULL, or [2] static global scales of x and of GEMM2's input
   // caller tensors
   const uint16_t* x;
   const float* logits;

@@ -74,6 +74,8 @@ struct moe_workspace {
   int32_t* inv;
   int4* tiles;
   int32_t* n_tiles;
+  float* act_scales;  // [2] static g_x, g_a (MOE_STATIC_ACT_SCALES)
+  bool act_scales_set;
   // intermediates
   float* act;
   float* act_amax;
@@ -120,6 +122,7 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->inv), R * 4);
   f(reinterpret_cast<void**>(&w->tiles), w->max_tiles_cap * 16);
   f(reinterpret_cast<void**>(&w->n_tiles), 4);
+  f(reinterpret_cast<void**>(&w->act_scales), 2 * 4);
   f(reinterpret_cast<void**>(&w->act), R * I * 4);
   f(reinterpret_cast<void**>(&w->act_amax), R * n_amax * 4);
   f(reinterpret_cast<void**>(&w->a2_codes), R * I / 2);
@@ -253,7 +256,7 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
     return fail(NVFP4_ERR_INVALID_ARG, "num_experts must be in [1, %d]", nvfp4::kMaxExperts);
   if (c.top_k < 1 || c.top_k > nvfp4::kMaxTopK || c.top_k > c.num_experts)
     return fail(NVFP4_ERR_INVALID_ARG, "top_k must be in [1, min(%d, num_experts)]", nvfp4::kMaxTopK);
-  if ((c.flags & ~MOE_DETERMINISTIC_FINALIZE) != 0)
+  if ((c.flags & ~(MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES)) != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "unknown flags 0x%x", c.flags);
   if (c.max_num_tokens * c.top_k > (int64_t(1) << 30))
     return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * top_k too large");
@@ -329,6 +332,17 @@ int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* 
   return ok();
 }
 
+int moe_workspace_set_act_scales(moe_workspace* ws, const float* scales_dev, void* stream) {
+  if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
+  if (!(ws->cfg.flags & MOE_STATIC_ACT_SCALES))
+    return fail(NVFP4_ERR_INVALID_ARG, "workspace was created without MOE_STATIC_ACT_SCALES");
+  if (!scales_dev || !aligned(scales_dev, 4)) return fail(NVFP4_ERR_INVALID_ARG, "NULL or misaligned scales");
+  hipError_t e = nvfp4::launch_copy_f32(scales_dev, ws->act_scales, 2, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "activation scale copy");
+  ws->act_scales_set = true;
+  return ok();
+}
+
 int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_dev, int64_t T,
                       void* out_dev, void* stream) {
   if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
@@ -338,6 +352,9 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
     return fail(NVFP4_ERR_TOO_MANY_TOKENS, "num_tokens (%lld) exceeds max_num_tokens (%lld)",
                 (long long)T, (long long)c.max_num_tokens);
   if (!ws->bound) return fail(NVFP4_ERR_NO_WEIGHTS, "no weights bound; call moe_workspace_bind_weights");
+  const bool static_scales = (c.flags & MOE_STATIC_ACT_SCALES) != 0;
+  if (static_scales && !ws->act_scales_set)
+    return fail(NVFP4_ERR_INVALID_ARG, "static activation scales not set; call moe_workspace_set_act_scales");
   if (T == 0) return ok();
   if (!x_dev || !logits_dev || !out_dev) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned(x_dev, 16) || !aligned(out_dev, 16) || !aligned(logits_dev, 4))
@@ -356,6 +373,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.R = static_cast<int>(T * c.top_k);
   nvfp4::choose_gemm(T, &p);
   p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
+  p.static_g = static_scales ? ws->act_scales : nullptr;
   p.x = static_cast<const uint16_t*>(x_dev);
   p.logits = logits_dev;
   p.out = static_cast<uint16_t*>(out_dev);

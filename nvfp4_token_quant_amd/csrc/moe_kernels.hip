@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   for (int lt = wave; lt < ntok; lt += 4) {
     const int64_t t = t0 + lt;
     quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
-                          p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr);
+                          p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
     route_token_wave<KPL>(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
                           s_ids + lt * k, lane);
     if (!p.deterministic) {
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
     const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * kSmallWaves + wave;
     if (t < T) {
       quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
-                            p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr);
+                            p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
       if (!p.deterministic) {
         float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
         for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
     __syncthreads();
     if (t >= T) return;
     const float* sq = s_am + 4 * q;
-    const float g = global_scale(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3])));
+    const float g = p.static_g ? p.static_g[0] : global_scale(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3])));
     uint8_t* crow = p.xq_codes + t * (H / 2);
     uint8_t* srow = p.xq_scales + t * (H / 16);
 #pragma unroll

@@ -47,8 +47,6 @@ __device__ __forceinline__ void load_row(RowRegs<NB>& rr, const uint16_t* __rest
   }
 }
 
-// Row amax -> g, then every block of the row; the block amaxes of the first
-// pass are reused by the second.
 // The dequantized values of one quantized block (code x block scale; exact
 // in fp16) as two 16-byte stores.
 __device__ __forceinline__ void store_block_f16(_Float16* dst, uint32_t lo, uint32_t hi, uint32_t sb) {
@@ -58,10 +56,14 @@ __device__ __forceinline__ void store_block_f16(_Float16* dst, uint32_t lo, uint
   d[1] = dequant8_f16(hi, sc);
 }
 
+// Row amax -> g, then every block of the row; the block amaxes of the first
+// pass are reused by the second.  gfix: NULL for the row's own global scale
+// 2688 / amax, else a given one.
 template <int NB>
 __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nblk, uint8_t* __restrict__ crow,
                                                   uint8_t* __restrict__ srow, float* __restrict__ gout,
-                                                  int lane, _Float16* __restrict__ x16row = nullptr) {
+                                                  int lane, _Float16* __restrict__ x16row = nullptr,
+                                                  const float* gfix = nullptr) {
   float bam[NB];
   float am = 0.0f;
 #pragma unroll
@@ -69,7 +71,7 @@ __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nbl
     bam[i] = amax16_bf16(rr.v[i][0], rr.v[i][1]);
     if (lane + kWave * i < nblk) am = fmaxf(am, bam[i]);
   }
-  const float g = global_scale(wave_max(am));
+  const float g = gfix ? *gfix : global_scale(wave_max(am));
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int b = lane + kWave * i;
@@ -89,11 +91,12 @@ __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nbl
 template <int NB>
 __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
                                   uint8_t* __restrict__ crow, uint8_t* __restrict__ srow,
-                                  float* __restrict__ gout, int lane, _Float16* __restrict__ x16row = nullptr) {
+                                  float* __restrict__ gout, int lane, _Float16* __restrict__ x16row = nullptr,
+                                  const float* gfix = nullptr) {
   if constexpr (NB > 0) {
     RowRegs<NB> rr;
     load_row<NB>(rr, xrow, nblk, lane);
-    quantize_row_regs<NB>(rr, nblk, crow, srow, gout, lane, x16row);
+    quantize_row_regs<NB>(rr, nblk, crow, srow, gout, lane, x16row, gfix);
   } else {
     // Rows too long for the register cache: amax pass, then quantize pass.
     float am = 0.0f;
@@ -101,7 +104,7 @@ __device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
       const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
       am = fmaxf(am, amax16_bf16(p[0], p[1]));
     }
-    const float g = global_scale(wave_max(am));
+    const float g = gfix ? *gfix : global_scale(wave_max(am));
     for (int b = lane; b < nblk; b += kWave) {
       const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * b);
       float f[16];
