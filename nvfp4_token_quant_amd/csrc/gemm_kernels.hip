@@ -41,19 +41,37 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
+// Workgroup barrier for LDS data only.  A full __syncthreads also waits for
+// every outstanding global load and store (the global->LDS copies count as
+// loads), which would drain the weight prefetch or wait for output stores;
+// here the caller has already waited for the copies it needs, this wave's
+// LDS accesses are complete (lgkmcnt 0), and the memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------
 // Epilogues.
 // ---------------------------------------------------------------------------
 
 // GEMM1: per lane, fragment pair (gate fh, up fh) holds h[n = c0 + 16 fh + 4g + i]
-// for row m = 16 fm + r16; ginv[fm] = 1 / (that row's token global scale).
+// for row m = 16 fm + r16; ginv[fm] = 1 / (that row's token global scale),
+// wginv = 1 / (the expert's W13 global scale).
 // act = silu(h_gate) * h_up in fp32, stored with the row's amax over these
 // columns in s_amax[wave][m].
 template <int FM, int FNH, int SM = 16 * FM>
 __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&acc)[2 * FNH][FM],
                                             int e, int row0, int nrows, int c0, const float (&ginv)[FM],
-                                            float (*s_amax)[SM], int wave, int g, int r16) {
-  const float wginv = 1.0f / p.w13g[e];
+                                            float (*s_amax)[SM], int wave, int g, int r16, float wginv) {
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int m = fm * 16 + r16;
@@ -88,7 +106,7 @@ __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&ac
 template <int MT>
 __device__ __forceinline__ void g1_store_band_amax(const FwdParams& p, float (*s_amax)[MT], int row0,
                                                    int nrows, int band, int nbands) {
-  __syncthreads();
+  lds_barrier();  // s_amax complete (the act stores need not be)
   if (threadIdx.x < MT && static_cast<int>(threadIdx.x) < nrows) {
     const int m = threadIdx.x;
     const float v = fmaxf(fmaxf(s_amax[0][m], s_amax[1][m]), fmaxf(s_amax[2][m], s_amax[3][m]));
@@ -112,12 +130,11 @@ __device__ __forceinline__ uint32_t requant_block(const float* __restrict__ src,
 
 // GEMM2: per lane, fragment f holds y[n = n0 + 16 f + 4g + i] of row m =
 // 16 fm + r16; ginv[fm] = 1 / (that row's a2 global scale), slot[fm] = its
-// t*k+j (atomic finalize only).
+// t*k+j (atomic finalize only), wginv = 1 / (the expert's W2 global scale).
 template <int FM, int FN>
 __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&acc)[FN][FM], int e,
                                             int row0, int nrows, int n0, const float (&ginv)[FM],
-                                            const int (&slot)[FM], int g, int r16) {
-  const float wginv = 1.0f / p.w2g[e];
+                                            const int (&slot)[FM], int g, int r16, float wginv) {
   const int H = p.H;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   }
   if (MODE == 0) {
     if (kp == 0) {
-      g1_epilogue<FM, 2>(p, acc, e, row0, nrows, 32 * j, ginv, s_amax, wave, g, r16);
+      g1_epilogue<FM, 2>(p, acc, e, row0, nrows, 32 * j, ginv, s_amax, wave, g, r16, 1.0f / p.w13g[e]);
     } else {
       if (g == 0)
 #pragma unroll
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     }
     g1_store_band_amax<MT>(p, s_amax, row0, nrows, blockIdx.y, gridDim.y);
   } else if (kp == 0) {
-    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
+    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16, 1.0f / p.w2g[e]);
   }
 }
 
@@ -476,24 +493,6 @@ constexpr int kTiledWaves = 4;
 constexpr int kTiledThreads = kTiledWaves * kWave;
 constexpr int kTiledRows = 128;  // rows of a tile (8 groups of 16)
 constexpr int kRefillOps = kUnitFrags + 1;  // vector memory instructions of load_unit_step
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
-// Workgroup barrier for the LDS operand only.  A full __syncthreads also
-// waits for every outstanding global load (the global->LDS copies count as
-// such), which would drain the weight prefetch; here the caller has already
-// waited for the copies it needs, this wave's LDS reads are complete
-// (lgkmcnt 0), and the memory clobber keeps the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Rows of the token operand for local row m of a tile: GEMM1 reads the
 // per-token quantized activations of token perm[row] / k, GEMM2 the
@@ -602,23 +601,34 @@ struct TiledShared {
   int src[kTiledRows];
   int slot[kTiledRows];
   float ginv[kTiledRows];
+  float wginv;  // 1 / (the expert's weight global scale)
   float amax[kTiledWaves][kTiledRows];
   // per thread: the source offsets of its copy instructions (at most 8)
   int coff[kTiledThreads * (kTiledRows * 16 / kWave / kTiledWaves)] __attribute__((aligned(16)));
 };
 static_assert(sizeof(TiledShared) <= 80 * 1024, "two tiled blocks must share a CU's LDS");
 
+// What a tiled block works on.
+struct TiledBlock {
+  int e, row0, nrows, band, nb;
+  int K, S;            // reduction length and its K steps
+  int j;               // this wave's unit within the expert
+  bool has_unit;       // the last band of units may be partial
+  const uint8_t* rec;  // this wave's unit records
+};
+
 // One tile whose rows fit in FMV 16-row groups: the copies, MFMAs and
 // epilogue cover only those groups, so a tile of few rows costs in
 // proportion to its rows (FMV is the smallest of 1, 2, 3, 4, 6, 8 groups
 // that holds them).
 template <int FMV, int MODE>
-__device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, int e, int row0, int nrows,
-                                           int band, int nb) {
+__device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, const TiledBlock& b,
+                                           UnitStep (&wb)[2], float my_g, int my_slot, float wg) {
   constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
   static_assert(kTiledThreads * NCP <= sizeof(TiledShared::coff) / sizeof(int), "copy offset table");
-  const int K = MODE == 0 ? p.H : p.I;
-  const int S = ksteps(K);
+  const int row0 = b.row0, nrows = b.nrows, K = b.K, S = b.S, j = b.j;
+  const bool has_unit = b.has_unit;
+  const uint8_t* rec = b.rec;
   // token operand: GEMM1 gathers rows of xq16 [T, K]; GEMM2 reads the tile's
   // own rows of a2q16 [R, K] (offsets relative to the tile's first row)
   const __amdgpu_buffer_rsrc_t a16 =
@@ -627,11 +637,6 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = t & (kWave - 1);
   const int g = lane >> 4, r16 = lane & 15;
-  const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
-  const int j = band * kTiledWaves + wave;
-  const bool has_unit = j < upe;  // the last band of units may be partial
-  const uint8_t* rec = (MODE == 0 ? p.w13 : p.w2) +
-                       (static_cast<int64_t>(e) * upe + (has_unit ? j : 0)) * S * kRecBytes;
   uint8_t* lds0 = sh.lds[0];
   uint8_t* lds1 = sh.lds[1];
 
@@ -648,9 +653,18 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
     coff[u] = 2 * src * K + 64 * (c & 3) + 16 * (lane >> 4);
   }
   tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);  // (reads back this thread's own writes)
-  UnitStep wb[2];
-  load_unit_step(wb[0], rec, lane);
-  load_unit_step(wb[1], rec + static_cast<int64_t>(min(1, S - 1)) * kRecBytes, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  // Publish the rows' scales and slots and the expert's weight scale, loaded
+  // at the block's start, for the epilogue (the K loop's barriers make the
+  // stores visible).  The weight records of the first two steps were issued
+  // before everything else; the K loop's waits count one refill newer than
+  // the step's copies, so wait here for all of it, the first copies included.
+  if (t < kTiledRows) {
+    sh.ginv[t] = t < nrows ? 1.0f / my_g : 0.0f;
+    sh.slot[t] = my_slot;
+  }
+  if (t == 0) sh.wginv = 1.0f / wg;
+  wait_vmcnt<0>();
   __builtin_amdgcn_sched_barrier(0);
 
   f32x4 acc[kUnitFrags][FMV];
@@ -670,6 +684,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
 
   float ginv[FMV];
   int slots[FMV];
+  const float wginv = sh.wginv;
 #pragma unroll
   for (int fm = 0; fm < FMV; ++fm) {
     ginv[fm] = sh.ginv[fm * 16 + r16];
@@ -677,14 +692,14 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   }
   if (MODE == 0) {
     if (has_unit) {
-      g1_epilogue<FMV, 2, kTiledRows>(p, acc, e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16);
+      g1_epilogue<FMV, 2, kTiledRows>(p, acc, b.e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16, wginv);
     } else if (g == 0) {
 #pragma unroll
       for (int fm = 0; fm < FMV; ++fm) sh.amax[wave][fm * 16 + r16] = 0.0f;
     }
-    g1_store_band_amax<kTiledRows>(p, sh.amax, row0, nrows, band, nb);
+    g1_store_band_amax<kTiledRows>(p, sh.amax, row0, nrows, b.band, b.nb);
   } else if (has_unit) {
-    g2_epilogue<FMV, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16);
+    g2_epilogue<FMV, kUnitFrags>(p, acc, b.e, row0, nrows, 64 * j, ginv, slots, g, r16, wginv);
   }
 }
 
@@ -706,23 +721,58 @@ void moe_tiled_kernel(FwdParams p) {
   const int tile = (L & 7) * per_xcd + local;
   if (local >= per_xcd || tile >= ntiles) return;
   const int4 td = p.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
+  TiledBlock b;
+  b.e = td.x;
+  b.row0 = td.y;
+  b.nrows = td.z;
+  b.band = band;
+  b.nb = nb;
+  b.K = MODE == 0 ? p.H : p.I;
+  b.S = ksteps(b.K);
+  const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+  const int upe = MODE == 0 ? p.I / 32 : p.H / 64;
+  b.j = band * kTiledWaves + wave;
+  b.has_unit = b.j < upe;
+  b.rec = (MODE == 0 ? p.w13 : p.w2) +
+          (static_cast<int64_t>(b.e) * upe + (b.has_unit ? b.j : 0)) * b.S * kRecBytes;
 
-  tile_rows<MODE>(p, row0, nrows, kTiledRows, sh.src, sh.ginv, sh.slot);
-  __syncthreads();
-  const int groups = (nrows + 15) >> 4;
+  // Start-up, shortest dependency chains first: the first two steps' weight
+  // records need only the tile; GEMM1's token copies need the permutation
+  // (the rows' source tokens go to LDS for the copy offsets), GEMM2's need
+  // nothing more.  The rows' global scales and slots are loaded here and
+  // published by tiled_tile.
+  UnitStep wb[2];
+  load_unit_step(wb[0], b.rec, lane);
+  load_unit_step(wb[1], b.rec + static_cast<int64_t>(min(1, b.S - 1)) * kRecBytes, lane);
+  float my_g = 1.0f;
+  int my_slot = -1;
+  if (MODE == 0) {
+    int src = -1;
+    if (t < b.nrows) {
+      my_slot = p.perm[b.row0 + t];
+      src = my_slot / p.k;
+      my_g = p.xq_g[src];
+    }
+    if (t < kTiledRows) sh.src[t] = src;
+    lds_barrier();
+  } else if (t < b.nrows) {
+    my_g = p.a2_g[b.row0 + t];
+    my_slot = p.perm[b.row0 + t];
+  }
+  const float wg = MODE == 0 ? p.w13g[b.e] : p.w2g[b.e];
+  const int groups = (b.nrows + 15) >> 4;
   if (groups > 6)
-    tiled_tile<8, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<8, MODE>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 4)
-    tiled_tile<6, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<6, MODE>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 3)
-    tiled_tile<4, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<4, MODE>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 2)
-    tiled_tile<3, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<3, MODE>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 1)
-    tiled_tile<2, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<2, MODE>(p, sh, b, wb, my_g, my_slot, wg);
   else
-    tiled_tile<1, MODE>(p, sh, e, row0, nrows, band, nb);
+    tiled_tile<1, MODE>(p, sh, b, wb, my_g, my_slot, wg);
 }
 
 // ---------------------------------------------------------------------------
