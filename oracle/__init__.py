@@ -226,6 +226,33 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, stati
     return (out, dbg) if debug else out
 
 
+def moe_layer_shared(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, shared: QuantWeights,
+                     strategy="sum", static_scales=None):
+    """Routed output plus a shared expert's output for the listed tokens.
+
+    [P3] Command-A-Plus multi-stream page, Cohere2MoeSparseMoeBlock.forward:
+    the shared expert runs on the same input as the routed experts, the two
+    outputs are added, and the 'average' combination strategy halves the sum.
+    The shared expert is an NVFP4 expert of the routed experts' shape applied
+    to every token with weight 1, its input quantized per token exactly as
+    the routed experts' (the same Q of x, the same re-quantization of its
+    act): it is the routed layer with one slot per token, all routed to it.
+    shared: QuantWeights holding that one expert (any expert id).
+    strategy: "sum" or "average".
+    """
+    if strategy not in ("sum", "average"):
+        raise ValueError("strategy must be 'sum' or 'average'")
+    if shared.experts.size != 1:
+        raise ValueError("shared holds exactly one expert")
+    x_bf16 = _c(x_bf16, np.uint16)
+    routed = moe_layer(x_bf16, ids, w, tokens, H, I, qw, static_scales=static_scales)
+    T = x_bf16.shape[0]
+    ids_s = np.full((T, 1), shared.experts[0], np.int32)
+    w_s = np.ones((T, 1), np.float64)
+    out = routed + moe_layer(x_bf16, ids_s, w_s, tokens, H, I, shared, static_scales=static_scales)
+    return out / 2 if strategy == "average" else out
+
+
 def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g, static_scales=None):
     x_bf16 = _c(x_bf16, np.uint16)
     ids = _c(ids, np.int32)
