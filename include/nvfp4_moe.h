@@ -115,13 +115,28 @@ int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, in
  * saturate (E4M3 block scale 448, E2M1 code 6). */
 #define MOE_STATIC_ACT_SCALES 0x2u
 
+/* Shared expert.  [P3] Command-A-Plus multi-stream page,
+ * Cohere2MoeSparseMoeBlock.forward: a shared expert runs on the same input
+ * as the routed experts and the layer returns routed + shared, halved under
+ * the 'average' combination strategy.  With MOE_SHARED_EXPERT the weights
+ * hold num_experts + 1 experts and the last one is the shared expert: an
+ * NVFP4 SwiGLU expert of the routed shape applied to every token with weight
+ * 1, its input quantized per token like the routed experts' (it joins the
+ * grouped GEMMs as one more group of T rows).  The router still chooses
+ * among the first num_experts (logits stay [T, num_experts]).  The finalize
+ * adds it to the weighted routed sum: out = bf16(c * (sum_j w_j y_j + y_s)),
+ * c = 1, or 0.5 with MOE_SHARED_AVERAGE (which requires MOE_SHARED_EXPERT).
+ * The deterministic finalize adds y_s after the k routed terms. */
+#define MOE_SHARED_EXPERT 0x4u
+#define MOE_SHARED_AVERAGE 0x8u
+
 typedef struct moe_config {
   int64_t max_num_tokens; /* token ceiling: every buffer is sized from it once */
   int64_t hidden;         /* H: multiple of 128 */
   int64_t inter;          /* I: multiple of 128 */
-  int32_t num_experts;    /* E: 1..1024 */
+  int32_t num_experts;    /* E: routed experts, 1..1024 */
   int32_t top_k;          /* k: 1..min(16, E) */
-  uint32_t flags;         /* MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES, or 0 */
+  uint32_t flags;         /* OR of the MOE_* flags above, or 0 */
 } moe_config;
 
 /* NVFP4 expert weights, device pointers.  w13 rows [0, I) are the gate
@@ -130,7 +145,8 @@ typedef struct moe_config {
  *   w13_gscale f32 [E]                            (per-expert global scale)
  *   w2_codes   u8 [E, H, I/2],  16-byte aligned   w2_scales  u8 [E, H, I/16]
  *   w2_gscale  f32 [E]
- * The dims must equal the workspace's (E, H, I). */
+ * The dims must equal the workspace's: num_experts = E, or E + 1 with
+ * MOE_SHARED_EXPERT (expert E is the shared one), and (H, I). */
 typedef struct moe_nvfp4_weights {
   int64_t num_experts, hidden, inter;
   const void* w13_codes;
@@ -241,9 +257,12 @@ int moe_token_ceiling(int64_t max_prefill, int64_t piecewise_max, int64_t graph_
  *   MOE_BUF_TOPK_W    f32 [T, k]      MOE_BUF_COUNTS    i32 [E]
  *   MOE_BUF_OFFSETS   i32 [E + 1]     MOE_BUF_PERM      i32 [T*k] (row -> t*k+j)
  *   MOE_BUF_INV       i32 [T*k]       ((t*k+j) -> row)
- *   MOE_BUF_ACT       f32 [T*k, I]    SwiGLU output per expanded row
- *   MOE_BUF_A2_CODES  u8 [T*k, I/2]   MOE_BUF_A2_SCALES u8 [T*k, I/16]
- *   MOE_BUF_A2_GSCALE f32 [T*k]       re-quantized activation
+ *   MOE_BUF_ACT       f32 [Rt, I]     SwiGLU output per expanded row
+ *   MOE_BUF_A2_CODES  u8 [Rt, I/2]    MOE_BUF_A2_SCALES u8 [Rt, I/16]
+ *   MOE_BUF_A2_GSCALE f32 [Rt]        re-quantized activation
+ * where Rt = T*k, plus T with MOE_SHARED_EXPERT: rows [0, T*k) are the
+ * routed rows in expert order, row T*k + t the shared expert's row of token
+ * t.
  * (sizes are reported for max_num_tokens rows)
  */
 typedef enum moe_buffer_id {

@@ -21,6 +21,8 @@ HEADERS = [os.path.join(ROOT, "include", "nvfp4_moe.h"), os.path.join(ROOT, "inc
 
 MOE_DETERMINISTIC_FINALIZE = 0x1
 MOE_STATIC_ACT_SCALES = 0x2
+MOE_SHARED_EXPERT = 0x4
+MOE_SHARED_AVERAGE = 0x8
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARG", 2: "NVFP4_ERR_TOO_MANY_TOKENS",
           3: "NVFP4_ERR_ALIAS", 4: "NVFP4_ERR_NO_WEIGHTS", 5: "NVFP4_ERR_METADATA_CHANGED",
@@ -231,9 +233,15 @@ class MoeLayer:
     """Workspace + bound weights.  forward(x, logits) -> bf16 [T, H]."""
 
     def __init__(self, max_num_tokens, hidden, inter, num_experts, top_k, deterministic=True,
-                 stream=None, static_act_scales=False):
+                 stream=None, static_act_scales=False, shared_expert=None):
+        """shared_expert: None, "sum" or "average" (the weights then hold
+        num_experts + 1 experts, the last one shared by every token)."""
+        if shared_expert not in (None, "sum", "average"):
+            raise ValueError("shared_expert must be None, 'sum' or 'average'")
         flags = (MOE_DETERMINISTIC_FINALIZE if deterministic else 0) | \
-            (MOE_STATIC_ACT_SCALES if static_act_scales else 0)
+            (MOE_STATIC_ACT_SCALES if static_act_scales else 0) | \
+            (MOE_SHARED_EXPERT if shared_expert else 0) | \
+            (MOE_SHARED_AVERAGE if shared_expert == "average" else 0)
         self.cfg = MoeConfig(max_num_tokens, hidden, inter, num_experts, top_k, flags)
         h = ctypes.c_void_p()
         _check(lib().moe_workspace_create(ctypes.byref(self.cfg), _stream(stream), ctypes.byref(h)))

@@ -150,8 +150,8 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
       if (p.deterministic) {
         *reinterpret_cast<float4*>(p.y + row * H + n) = make_float4(y0, y1, y2, y3);
       } else {
-        const float w = p.topk_w[slot[fm]];
-        float* dst = p.out_acc + static_cast<int64_t>(slot[fm] / p.k) * H + n;
+        const float w = slot_weight(p, slot[fm]);
+        float* dst = p.out_acc + static_cast<int64_t>(slot_token(p, slot[fm])) * H + n;
         atomicAdd(dst + 0, w * y0);
         atomicAdd(dst + 1, w * y1);
         atomicAdd(dst + 2, w * y2);
@@ -304,10 +304,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     // Source rows of the tile.  The row table load goes first, so that
     // waiting for it does not wait for weights.
     int src = 0;
-    if (lane < nrows) slot = p.perm[row0 + lane];
+    if (lane < nrows) slot = row_slot(p, row0 + lane);
 #pragma unroll
     for (int d = 0; d < kStreamEarly; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-    if (lane < nrows) src = slot / p.k;
+    if (lane < nrows) src = slot_token(p, slot);
     const int cbytes = K / 2, sbytes = K / 16;
     for (int m = wave; m < nrows; m += 4) {
       const int64_t sm = __builtin_amdgcn_readlane(src, m);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-    if (!p.deterministic && lane < nrows) slot = p.perm[row0 + lane];
+    if (!p.deterministic && lane < nrows) slot = row_slot(p, row0 + lane);
     // row global scales g2 = 2688 / amax(act row)
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -505,8 +505,8 @@ __device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrow
     int src = -1, slot = -1;
     float gi = 0.0f;
     if (m < nrows) {
-      slot = p.perm[row0 + m];
-      src = MODE == 0 ? slot / p.k : row0 + m;
+      slot = row_slot(p, row0 + m);
+      src = MODE == 0 ? slot_token(p, slot) : row0 + m;
       gi = 1.0f / (MODE == 0 ? p.xq_g[src] : p.a2_g[src]);
     }
     s_src[m] = src;
@@ -749,15 +749,15 @@ void moe_tiled_kernel(FwdParams p) {
   if (MODE == 0) {
     int src = -1;
     if (t < b.nrows) {
-      my_slot = p.perm[b.row0 + t];
-      src = my_slot / p.k;
+      my_slot = row_slot(p, b.row0 + t);
+      src = slot_token(p, my_slot);
       my_g = p.xq_g[src];
     }
     if (t < kTiledRows) sh.src[t] = src;
     lds_barrier();
   } else if (t < b.nrows) {
     my_g = p.a2_g[b.row0 + t];
-    my_slot = p.perm[b.row0 + t];
+    my_slot = row_slot(p, b.row0 + t);
   }
   const float wg = MODE == 0 ? p.w13g[b.e] : p.w2g[b.e];
   const int groups = (b.nrows + 15) >> 4;
@@ -784,7 +784,7 @@ void moe_tiled_kernel(FwdParams p) {
 __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
-  if (row >= p.R) return;
+  if (row >= p.Rt) return;
   const int I = p.I;
   float a = 0.0f;
   for (int j = lane; j < p.g1_bands; j += kWave) a = fmaxf(a, p.act_amax[row * p.g1_bands + j]);
@@ -900,7 +900,7 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     const int gx = (max_tiles + 7) / 8 * 8;  // == p.tiled_gx
     moe_tiled_kernel<0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
     if (ev) (void)hipEventRecord(ev[2], s);
-    moe_requant_kernel<<<(p.R + 3) / 4, 256, 0, s>>>(p);
+    moe_requant_kernel<<<(p.Rt + 3) / 4, 256, 0, s>>>(p);
     moe_tiled_kernel<1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
     if (ev) (void)hipEventRecord(ev[3], s);
   }

@@ -54,7 +54,12 @@ __host__ __device__ constexpr int64_t packed_bytes(int64_t units, int K) {
 enum GemmKind { kGemmStream = 0, kGemmTiled = 1 };
 
 struct FwdParams {
-  int T, H, I, E, k, R;
+  // R = T*k routed expanded rows [0, R), in expert order.  With a shared
+  // expert (shared = 1) the rows [R, R + T) follow: row R + t is token t
+  // applied to expert E; Rt is the total.
+  int T, H, I, E, k, R, Rt;
+  int shared;         // 1: expert E is applied to every token with weight 1
+  float combine;      // output scale: 1 (routed + shared), 0.5 ('average')
   int mt;             // rows per M-tile of the grouped GEMMs
   int gemm_kind;      // GemmKind
   int g1_ks, g2_ks;   // stream kernels: waves sharing one unit's K range (1, 2, 4)
@@ -78,18 +83,18 @@ struct FwdParams {
   int32_t* blk_counts;  // [nblocks, E] per-block counts, then per-block bases
   int32_t* counts;      // [E]
   int32_t* offsets;     // [E+1]
-  int32_t* perm;        // [R] row -> t*k+j
+  int32_t* perm;        // [R] routed row -> t*k+j
   int32_t* inv;         // [R] t*k+j -> row
   int4* tiles;          // [max_tiles] (expert, row0, nrows, 0)
   int32_t* n_tiles;     // device scalar
   // intermediates
-  float* act;       // [R, I]
-  float* act_amax;  // [R, g1_bands <= I / 32] partial row amax per GEMM1 column band
+  float* act;       // [Rt, I]
+  float* act_amax;  // [Rt, g1_bands <= I / 32] partial row amax per GEMM1 column band
   uint8_t* a2_codes;
   uint8_t* a2_scales;
   float* a2_g;
-  _Float16* a2q16;  // [R, I] dequantized re-quantized act (exact in fp16); tiled path only
-  float* y;        // [R, H] (deterministic finalize)
+  _Float16* a2q16;  // [Rt, I] dequantized re-quantized act (exact in fp16); tiled path only
+  float* y;        // [Rt, H] (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
   // weights: unit records (see kRecBytes) and per-expert global scales
   const uint8_t* w13;
@@ -98,6 +103,27 @@ struct FwdParams {
   const float* w2g;
   const uint8_t* dummy;  // kRecBytes of zeros: target of loads past a wave's last K step
 };
+
+// Expanded-row helpers.  A routed row's slot is t*k + j (from perm); a
+// shared row's slot is the row itself (>= R), so one int names every row's
+// token and output weight.
+__device__ __forceinline__ int row_slot(const FwdParams& p, int row) { return row < p.R ? p.perm[row] : row; }
+__device__ __forceinline__ int slot_token(const FwdParams& p, int slot) {
+  return slot < p.R ? slot / p.k : slot - p.R;
+}
+// weight of a slot in the output sum, the combination scale included
+__device__ __forceinline__ float slot_weight(const FwdParams& p, int slot) {
+  return slot < p.R ? p.topk_w[slot] * p.combine : p.combine;
+}
+// Append the shared expert's tiles (rows R .. R + T - 1, expert E) after the
+// routed tiles; returns the new tile count.  Called by one thread.
+__device__ __forceinline__ int append_shared_tiles(const FwdParams& p, int ntiles) {
+  if (!p.shared) return ntiles;
+  const int nt = (p.T + p.mt - 1) / p.mt;
+  for (int i = 0; i < nt; ++i)
+    p.tiles[ntiles + i] = make_int4(p.E, p.R + i * p.mt, min(p.mt, p.T - i * p.mt), 0);
+  return ntiles + nt;
+}
 
 // quantize.hip
 int quant_nb_for_cols(int64_t cols);

@@ -100,12 +100,20 @@ struct moe_workspace {
 
 namespace {
 
+bool has_shared(const moe_config& c) { return (c.flags & MOE_SHARED_EXPERT) != 0; }
+// expanded rows of the shared expert (one per token of the ceiling)
+int64_t shared_rows(const moe_config& c) { return has_shared(c) ? c.max_num_tokens : 0; }
+// experts held by the weight buffers (the shared one last)
+int64_t weight_experts(const moe_config& c) { return c.num_experts + (has_shared(c) ? 1 : 0); }
+
 // Every buffer the workspace owns, in one list for allocation and release.
 template <typename F>
 void for_each_buffer(moe_workspace* w, F&& f) {
   const moe_config& c = w->cfg;
   const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, k = c.top_k;
-  const int64_t R = T * k;
+  const int64_t R = T * k;               // routed rows
+  const int64_t Rt = R + shared_rows(c);  // GEMM rows
+  const int64_t Ew = weight_experts(c);
   const int64_t n_amax = I / 32;  // GEMM1 column bands of 32 (the finest band used)
   const bool det = (c.flags & MOE_DETERMINISTIC_FINALIZE) != 0;
   f(reinterpret_cast<void**>(&w->xq_codes), T * H / 2);
@@ -123,18 +131,18 @@ void for_each_buffer(moe_workspace* w, F&& f) {
   f(reinterpret_cast<void**>(&w->tiles), w->max_tiles_cap * 16);
   f(reinterpret_cast<void**>(&w->n_tiles), 4);
   f(reinterpret_cast<void**>(&w->act_scales), 2 * 4);
-  f(reinterpret_cast<void**>(&w->act), R * I * 4);
-  f(reinterpret_cast<void**>(&w->act_amax), R * n_amax * 4);
-  f(reinterpret_cast<void**>(&w->a2_codes), R * I / 2);
-  f(reinterpret_cast<void**>(&w->a2_scales), R * I / 16);
-  f(reinterpret_cast<void**>(&w->a2_g), R * 4);
-  f(reinterpret_cast<void**>(&w->a2q16), R * I * 2);
-  f(reinterpret_cast<void**>(&w->y), det ? R * H * 4 : 0);
+  f(reinterpret_cast<void**>(&w->act), Rt * I * 4);
+  f(reinterpret_cast<void**>(&w->act_amax), Rt * n_amax * 4);
+  f(reinterpret_cast<void**>(&w->a2_codes), Rt * I / 2);
+  f(reinterpret_cast<void**>(&w->a2_scales), Rt * I / 16);
+  f(reinterpret_cast<void**>(&w->a2_g), Rt * 4);
+  f(reinterpret_cast<void**>(&w->a2q16), Rt * I * 2);
+  f(reinterpret_cast<void**>(&w->y), det ? Rt * H * 4 : 0);
   f(reinterpret_cast<void**>(&w->out_acc), det ? 0 : T * H * 4);
-  f(reinterpret_cast<void**>(&w->w13), nvfp4::packed_bytes(nvfp4::w13_units(E, I), static_cast<int>(H)));
-  f(reinterpret_cast<void**>(&w->w2), nvfp4::packed_bytes(nvfp4::w2_units(E, H), static_cast<int>(I)));
-  f(reinterpret_cast<void**>(&w->w13g), E * 4);
-  f(reinterpret_cast<void**>(&w->w2g), E * 4);
+  f(reinterpret_cast<void**>(&w->w13), nvfp4::packed_bytes(nvfp4::w13_units(Ew, I), static_cast<int>(H)));
+  f(reinterpret_cast<void**>(&w->w2), nvfp4::packed_bytes(nvfp4::w2_units(Ew, H), static_cast<int>(I)));
+  f(reinterpret_cast<void**>(&w->w13g), Ew * 4);
+  f(reinterpret_cast<void**>(&w->w2g), Ew * 4);
   f(reinterpret_cast<void**>(&w->dummy), nvfp4::kRecBytes);
 }
 
@@ -145,17 +153,21 @@ void free_all(moe_workspace* w) {
   });
 }
 
-int64_t tiles_bound(int64_t R, int64_t E, int mt) { return (R + mt - 1) / mt + std::min(E, R); }
+// Tiles of R routed rows over E experts, plus those of the shared expert's
+// T rows (shared_T = 0 without one).
+int64_t tiles_bound(int64_t R, int64_t E, int mt, int64_t shared_T) {
+  return (R + mt - 1) / mt + std::min(E, R) + (shared_T + mt - 1) / mt;
+}
 
 int check_weights_desc(const moe_workspace* ws, const moe_nvfp4_weights* w, bool need_codes) {
   if (!w) return fail(NVFP4_ERR_INVALID_ARG, "weights descriptor is NULL");
   const moe_config& c = ws->cfg;
-  if (w->num_experts != c.num_experts || w->hidden != c.hidden || w->inter != c.inter)
+  if (w->num_experts != weight_experts(c) || w->hidden != c.hidden || w->inter != c.inter)
     return fail(NVFP4_ERR_METADATA_CHANGED,
-                "weight dims (E=%lld, H=%lld, I=%lld) differ from the workspace's (E=%d, H=%lld, "
+                "weight dims (E=%lld, H=%lld, I=%lld) differ from the workspace's (E=%lld, H=%lld, "
                 "I=%lld); recapture is required",
-                (long long)w->num_experts, (long long)w->hidden, (long long)w->inter, c.num_experts,
-                (long long)c.hidden, (long long)c.inter);
+                (long long)w->num_experts, (long long)w->hidden, (long long)w->inter,
+                (long long)weight_experts(c), (long long)c.hidden, (long long)c.inter);
   if (!w->w13_scales || !w->w2_scales || !w->w13_gscale || !w->w2_gscale)
     return fail(NVFP4_ERR_INVALID_ARG, "weight scale pointers must be non-NULL");
   if (!aligned(w->w13_gscale, 4) || !aligned(w->w2_gscale, 4))
@@ -174,7 +186,7 @@ int check_weights_desc(const moe_workspace* ws, const moe_nvfp4_weights* w, bool
 hipError_t copy_weights(moe_workspace* ws, const moe_nvfp4_weights* w, const void* w13c,
                         const void* w2c, hipStream_t s) {
   const moe_config& c = ws->cfg;
-  const int64_t E = c.num_experts, H = c.hidden, I = c.inter;
+  const int64_t E = weight_experts(c), H = c.hidden, I = c.inter;
   hipError_t e = nvfp4::launch_pack_weights(static_cast<const uint8_t*>(w13c),
                                             static_cast<const uint8_t*>(w->w13_scales), ws->w13, E,
                                             2 * I, H, 1, s);
@@ -256,10 +268,15 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
     return fail(NVFP4_ERR_INVALID_ARG, "num_experts must be in [1, %d]", nvfp4::kMaxExperts);
   if (c.top_k < 1 || c.top_k > nvfp4::kMaxTopK || c.top_k > c.num_experts)
     return fail(NVFP4_ERR_INVALID_ARG, "top_k must be in [1, min(%d, num_experts)]", nvfp4::kMaxTopK);
-  if ((c.flags & ~(MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES)) != 0)
+  if ((c.flags & ~(MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES | MOE_SHARED_EXPERT |
+                   MOE_SHARED_AVERAGE)) != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "unknown flags 0x%x", c.flags);
-  if (c.max_num_tokens * c.top_k > (int64_t(1) << 30))
-    return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * top_k too large");
+  if ((c.flags & MOE_SHARED_AVERAGE) && !(c.flags & MOE_SHARED_EXPERT))
+    return fail(NVFP4_ERR_INVALID_ARG, "MOE_SHARED_AVERAGE requires MOE_SHARED_EXPERT");
+  if (c.num_experts + ((c.flags & MOE_SHARED_EXPERT) ? 1 : 0) > nvfp4::kMaxExperts)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_experts plus the shared expert must be <= %d", nvfp4::kMaxExperts);
+  if (c.max_num_tokens * (c.top_k + 1) > (int64_t(1) << 30))
+    return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * (top_k + 1) too large");
   if (c.max_num_tokens * c.hidden >= (int64_t(1) << 30))
     return fail(NVFP4_ERR_INVALID_ARG, "max_num_tokens * hidden must be < 2^30 (got %lld)",
                 (long long)(c.max_num_tokens * c.hidden));
@@ -272,7 +289,7 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
     return fail(NVFP4_ERR_HIP, "hipGetDevice failed");
   }
   const int64_t Rmax = c.max_num_tokens * c.top_k;
-  w->max_tiles_cap = tiles_bound(Rmax, c.num_experts, 16);
+  w->max_tiles_cap = tiles_bound(Rmax, c.num_experts, 16, shared_rows(c));
   w->route_blocks_cap = static_cast<int>(std::max<int64_t>(
       nvfp4::kMaxRouteBlocks,
       (c.max_num_tokens + nvfp4::kMaxTokensPerRouteBlock - 1) / nvfp4::kMaxTokensPerRouteBlock));
@@ -371,6 +388,9 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.E = static_cast<int>(E);
   p.k = c.top_k;
   p.R = static_cast<int>(T * c.top_k);
+  p.shared = has_shared(c) ? 1 : 0;
+  p.Rt = p.R + (p.shared ? p.T : 0);
+  p.combine = (c.flags & MOE_SHARED_AVERAGE) ? 0.5f : 1.0f;
   nvfp4::choose_gemm(T, &p);
   p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
   p.static_g = static_scales ? ws->act_scales : nullptr;
@@ -405,7 +425,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.w2 = ws->w2;
   p.w2g = ws->w2g;
   p.dummy = ws->dummy;
-  const int64_t max_tiles = tiles_bound(p.R, E, p.mt);
+  const int64_t max_tiles = tiles_bound(p.R, E, p.mt, p.shared ? T : 0);
   p.tiled_gx = static_cast<int>((max_tiles + 7) / 8 * 8);
   if (max_tiles > ws->max_tiles_cap) return fail(NVFP4_ERR_INVALID_ARG, "internal: tile bound exceeds capacity");
   hipError_t e = nvfp4::launch_moe_forward(p, static_cast<int>(max_tiles), static_cast<hipStream_t>(stream),
@@ -452,6 +472,7 @@ int moe_workspace_buffer(const moe_workspace* ws, int32_t id, void** ptr_out, in
   if (!ws || !ptr_out || !bytes_out) return fail(NVFP4_ERR_INVALID_ARG, "NULL argument");
   const moe_config& c = ws->cfg;
   const int64_t T = c.max_num_tokens, H = c.hidden, I = c.inter, E = c.num_experts, R = T * c.top_k;
+  const int64_t Rt = R + shared_rows(c);
   void* p = nullptr;
   int64_t n = 0;
   switch (id) {
@@ -464,10 +485,10 @@ int moe_workspace_buffer(const moe_workspace* ws, int32_t id, void** ptr_out, in
     case MOE_BUF_OFFSETS: p = ws->offsets; n = (E + 1) * 4; break;
     case MOE_BUF_PERM: p = ws->perm; n = R * 4; break;
     case MOE_BUF_INV: p = ws->inv; n = R * 4; break;
-    case MOE_BUF_ACT: p = ws->act; n = R * I * 4; break;
-    case MOE_BUF_A2_CODES: p = ws->a2_codes; n = R * I / 2; break;
-    case MOE_BUF_A2_SCALES: p = ws->a2_scales; n = R * I / 16; break;
-    case MOE_BUF_A2_GSCALE: p = ws->a2_g; n = R * 4; break;
+    case MOE_BUF_ACT: p = ws->act; n = Rt * I * 4; break;
+    case MOE_BUF_A2_CODES: p = ws->a2_codes; n = Rt * I / 2; break;
+    case MOE_BUF_A2_SCALES: p = ws->a2_scales; n = Rt * I / 16; break;
+    case MOE_BUF_A2_GSCALE: p = ws->a2_g; n = Rt * 4; break;
     default: return fail(NVFP4_ERR_INVALID_ARG, "unknown buffer id %d", id);
   }
   *ptr_out = p;

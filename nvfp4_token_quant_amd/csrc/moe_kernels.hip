@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
     }
     if (tid == 255) {
       p.offsets[E] = s_part[255][0];
-      *p.n_tiles = s_part[255][1];
+      *p.n_tiles = append_shared_tiles(p, s_part[255][1]);
     }
   }
   const int i = blockIdx.x * 256 + tid;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   }
   if (tid == kSmallMaxE - 1) {
     p.offsets[E] = s_part[kSmallMaxE - 1][0];
-    *p.n_tiles = s_part[kSmallMaxE - 1][1];
+    *p.n_tiles = append_shared_tiles(p, s_part[kSmallMaxE - 1][1]);
   }
   __syncthreads();
   // 5. placement
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
     }
     if (tid == 0) {
       p.offsets[E] = rows_total;
-      *p.n_tiles = tiles_total;
+      *p.n_tiles = append_shared_tiles(p, tiles_total);
     }
   }
   __syncthreads();
@@ -634,6 +634,9 @@ static void launch_prologue_small(const FwdParams& p, hipStream_t s) {
 
 // Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[inv[t, j], n]) in slot
 // order (deterministic), or bf16_rne(out_acc[t, n]) after the atomic epilogue.
+// With a shared expert the deterministic sum adds its row R + t last and the
+// total is multiplied by the combination scale (1 or 0.5, exact); the atomic
+// epilogue applies the scale to each contribution.
 // One thread per 4 output columns; the slots are taken 8 at a time with all
 // their row-index, weight and y loads issued before the sums.
 __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
@@ -666,6 +669,13 @@ __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
           acc.w += w[j] * y[j].w;
         }
       }
+    }
+    if (p.shared) {
+      const float4 ys = *reinterpret_cast<const float4*>(p.y + (p.R + t) * H + n);
+      acc.x = (acc.x + ys.x) * p.combine;
+      acc.y = (acc.y + ys.y) * p.combine;
+      acc.z = (acc.z + ys.z) * p.combine;
+      acc.w = (acc.w + ys.w) * p.combine;
     }
   } else {
     acc = *reinterpret_cast<const float4*>(p.out_acc + t * H + n);

@@ -10,21 +10,24 @@ import numpy as np
 from . import binding, synth
 
 
-def gpu_weights(layer_id: int, device="cuda", chunk: int = 16):
-    """NVFP4 weights of every expert, generated and quantized on the device."""
+def gpu_weights(layer_id: int, device="cuda", chunk: int = 16, n_experts: int | None = None):
+    """NVFP4 weights of experts 0 .. n_experts - 1 (default: the layer's E;
+    E + 1 adds a shared expert, generated like the others), generated and
+    quantized on the device."""
     import torch
 
     L = synth.LAYERS[layer_id]
+    E = L.E if n_experts is None else n_experts
     (r13, c13), (r2, c2) = synth.weight_shapes(layer_id)
     k13 = synth.weight_key(layer_id, synth.WEIGHT_W13)
     k2 = synth.weight_key(layer_id, synth.WEIGHT_W2)
     out = []
     for key, (r, c) in ((k13, (r13, c13)), (k2, (r2, c2))):
-        codes = torch.empty((L.E, r, c // 2), dtype=torch.uint8, device=device)
-        scales = torch.empty((L.E, r, c // 16), dtype=torch.uint8, device=device)
-        g = torch.empty((L.E,), dtype=torch.float32, device=device)
-        for e0 in range(0, L.E, chunk):
-            n = min(chunk, L.E - e0)
+        codes = torch.empty((E, r, c // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((E, r, c // 16), dtype=torch.uint8, device=device)
+        g = torch.empty((E,), dtype=torch.float32, device=device)
+        for e0 in range(0, E, chunk):
+            n = min(chunk, E - e0)
             w = binding.synth_weights(*key, e0, n, (r, c), L.sigma, device=device)
             qc, qs, qg = binding.quantize_experts(w)
             codes[e0:e0 + n].copy_(qc)
