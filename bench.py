@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--fast-finalize", action="store_true",
                     help="atomic (non-deterministic) finalize instead of the slot-ordered one")
     ap.add_argument("--rotate", type=int, default=2, help="copies of the expert weights")
+    ap.add_argument("--shared", choices=["sum", "average"], default=None,
+                    help="add a shared expert (weights of E + 1 experts), combined as routed + shared "
+                         "or their average")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
@@ -135,7 +138,8 @@ def main():
     logits_np = synth.router_logits(args.layer, T)
     x = to_device_bf16(x_bits, dev)
     logits = torch.from_numpy(logits_np).to(dev)
-    weights = [gpu_weights(args.layer, device=dev)]
+    n_shared = 1 if args.shared else 0
+    weights = [gpu_weights(args.layer, device=dev, n_experts=E + n_shared)]
     for _ in range(args.rotate - 1):
         w0 = weights[0]
         weights.append(binding.NvFp4Weights(*(t.clone() for t in (
@@ -144,7 +148,7 @@ def main():
     max_tokens = max(T, L.max_tokens)
     layers = []
     for w in weights:
-        ly = binding.MoeLayer(max_tokens, H, I, E, k, deterministic=det)
+        ly = binding.MoeLayer(max_tokens, H, I, E, k, deterministic=det, shared_expert=args.shared)
         ly.bind(w)
         layers.append(ly)
     out = torch.empty_like(x)
@@ -154,12 +158,12 @@ def main():
     layers[0].forward_into(x, logits, out)
     torch.cuda.synchronize()
     counts = layers[0].read_buffer("COUNTS", torch.int32, (E,)).cpu().numpy()
-    active = int((counts > 0).sum())
-    R = T * k
+    active = int((counts > 0).sum()) + n_shared  # the shared expert counts as one more active expert
+    R = T * (k + n_shared)  # expanded rows through the GEMMs
     w13_bytes = 2 * I * H * 0.5625 + 4
     w2_bytes = H * I * 0.5625 + 4
     stage_bytes = {
-        "prologue": T * H * 2 + T * E * 4 + T * (H * 0.5625 + 4) + R * 8,
+        "prologue": T * H * 2 + T * E * 4 + T * (H * 0.5625 + 4) + T * k * 8,
         "gemm1": active * w13_bytes + R * (H * 0.5625 + 4),
         "gemm2": active * w2_bytes,
         "finalize": T * H * 2,
@@ -239,7 +243,7 @@ def main():
     tokens_per_s = T * args.steps / (t1 - t0)
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
-    workload = f"nvfp4_moe_layer_{L.name}"
+    workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "")
     traffic = measured_traffic(workload, T, dominant)
     mfma_bound = layer_flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > layer_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
@@ -260,7 +264,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, x_bits, T, H, I, k)
+        cpu = cpu_baseline(args, x_bits, T, H, I, k, L.E)
 
     for ly in layers:
         ly.close()
@@ -279,6 +283,7 @@ def main():
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
+                   "shared_expert": args.shared,
                    "weights_rotated": args.rotate,
                    "hip_graph": "one graph holding the timed forwards" if not args.eager else "none (eager)",
                    "parallelism": "none (1 GPU)"},
@@ -388,15 +393,23 @@ def cpu_baseline_quantize(args, x_bits):
             "sample": f"first {n} of {T} rows x {reps} repetitions ({dt:.1f} s)"}
 
 
-def cpu_baseline(args, x_bits, T, H, I, k):
+def cpu_baseline(args, x_bits, T, H, I, k, E):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
 
     import oracle
     from nvfp4_token_quant_amd import synth
-    from tests.layer_fixtures import oracle_weights
+    from tests.layer_fixtures import oracle_expert, oracle_weights
 
     ids, w = oracle.router(synth.router_logits(args.layer, T), k)
+    shared = None
+    if args.shared:
+        shared = oracle.QuantWeights(np.array([E], np.int32), *(a[None] for a in oracle_expert(args.layer, E)))
+
+    def run(toks, qw):
+        if shared is None:
+            return oracle.moe_layer(x_bits, ids, w, toks, H, I, qw)
+        return oracle.moe_layer_shared(x_bits, ids, w, toks, H, I, qw, shared, args.shared)
     rng = np.random.default_rng(0)
     n = T
     toks = np.arange(T)
@@ -404,7 +417,7 @@ def cpu_baseline(args, x_bits, T, H, I, k):
     probe = toks[: max(1, min(T, 4))]
     qw = oracle_weights(args.layer, np.unique(ids[probe]))
     t0 = time.perf_counter()
-    oracle.moe_layer(x_bits, ids, w, probe, H, I, qw)
+    run(probe, qw)
     t_probe = time.perf_counter() - t0
     n = int(min(T, max(len(probe), args.cpu_budget_s / max(t_probe / len(probe), 1e-6))))
     toks = np.sort(rng.choice(T, n, replace=False)) if n < T else toks
@@ -412,7 +425,7 @@ def cpu_baseline(args, x_bits, T, H, I, k):
     reps, dt = 0, 0.0
     while dt < args.cpu_budget_s * 0.8 or reps == 0:   # repeat small samples to ~the budget
         t0 = time.perf_counter()
-        oracle.moe_layer(x_bits, ids, w, toks, H, I, qw)
+        run(toks, qw)
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": reps * len(toks) / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
