@@ -529,13 +529,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tiled_rsrc(const _Float16* bas
 }
 
 template <int NCP>
-__device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const int* coff_lds, uint8_t* buf,
+__device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const int* coff, uint8_t* buf,
                                                 int s, int wave) {
-  // this lane's source byte offsets are kept in LDS to spare registers
+  // coff: this lane's source byte offsets of the NCP copies (registers)
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
     auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + kTiledWaves * u));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, coff_lds[u] + 256 * s, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, coff[u] + 256 * s, 0, 0, 0);
   }
 }
 
@@ -545,7 +545,7 @@ __device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const
 template <int FM, int NCP>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
                                            uint8_t* nxt, UnitStep& w, const uint8_t* rec, __amdgpu_buffer_rsrc_t a16,
-                                           const int* coff, bool has_unit, int wave, int lane) {
+                                           const int (&coff)[NCP], bool has_unit, int wave, int lane) {
   const int g = lane >> 4, r16 = lane & 15;
   wait_vmcnt<kRefillOps>();  // this step's copies have landed (see the kernel comment)
   lds_barrier();             // ... in every wave; the other buffer is free
@@ -603,8 +603,6 @@ struct TiledShared {
   float ginv[kTiledRows];
   float wginv;  // 1 / (the expert's weight global scale)
   float amax[kTiledWaves][kTiledRows];
-  // per thread: the source offsets of its copy instructions (at most 8)
-  int coff[kTiledThreads * (kTiledRows * 16 / kWave / kTiledWaves)] __attribute__((aligned(16)));
 };
 static_assert(sizeof(TiledShared) <= 80 * 1024, "two tiled blocks must share a CU's LDS");
 
@@ -625,7 +623,6 @@ template <int FMV, int MODE>
 __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, const TiledBlock& b,
                                            UnitStep (&wb)[2], float my_g, int my_slot, float wg) {
   constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
-  static_assert(kTiledThreads * NCP <= sizeof(TiledShared::coff) / sizeof(int), "copy offset table");
   const int row0 = b.row0, nrows = b.nrows, K = b.K, S = b.S, j = b.j;
   const bool has_unit = b.has_unit;
   const uint8_t* rec = b.rec;
@@ -643,7 +640,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   // this wave's copies: instruction u fills chunk c = wave + 4 u, i.e.
   // (fm, g) = (c / 4, c % 4); lane l brings bytes 64 g + 16 (l / 16) .. + 15
   // of the step's segment of tile row 16 fm + l % 16
-  int* coff = sh.coff + t * NCP;
+  int coff[NCP];
 #pragma unroll
   for (int u = 0; u < NCP; ++u) {
     const int c = wave + kTiledWaves * u;
@@ -652,7 +649,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
     const int src = MODE == 0 ? max(sh.src[r], 0) : (r < nrows ? r : 0);
     coff[u] = 2 * src * K + 64 * (c & 3) + 16 * (lane >> 4);
   }
-  tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);  // (reads back this thread's own writes)
+  tiled_copy_step<NCP>(a16, coff, lds0, 0, wave);
   __builtin_amdgcn_sched_barrier(0);
   // Publish the rows' scales and slots and the expert's weight scale, loaded
   // at the block's start, for the epilogue (the K loop's barriers make the
