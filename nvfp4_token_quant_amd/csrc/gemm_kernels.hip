@@ -528,15 +528,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tiled_rsrc(const _Float16* bas
                                            static_cast<int>(2 * elems), 0x00020000);
 }
 
+// One copy instruction: 16 bytes per lane from byte offset `off` of the
+// resource into 1 KB chunk `chunk` of the LDS buffer.
+__device__ __forceinline__ void tiled_copy_one(__amdgpu_buffer_rsrc_t rs, int off, uint8_t* buf, int chunk) {
+  auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * chunk);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
+}
+
 template <int NCP>
 __device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const int* coff, uint8_t* buf,
                                                 int s, int wave) {
   // coff: this lane's source byte offsets of the NCP copies (registers)
 #pragma unroll
-  for (int u = 0; u < NCP; ++u) {
-    auto* d = (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + kTiledWaves * u));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, coff[u] + 256 * s, 0, 0, 0);
-  }
+  for (int u = 0; u < NCP; ++u) tiled_copy_one(rs, coff[u] + 256 * s, buf, wave + kTiledWaves * u);
 }
 
 // One K step: wait for this step's copies, start the next step's, MFMAs on
@@ -549,13 +553,16 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
   const int g = lane >> 4, r16 = lane & 15;
   wait_vmcnt<kRefillOps>();  // this step's copies have landed (see the kernel comment)
   lds_barrier();             // ... in every wave; the other buffer is free
-  tiled_copy_step<NCP>(a16, coff, nxt, min(s + 1, S - 1), wave);  // (the last step's copy is unused)
-  __builtin_amdgcn_sched_barrier(0);
+  const int sn = min(s + 1, S - 1);  // the next step's copies (the last step's are unused)
   if (has_unit) {
     // The step's 4*FM (q, fm) token fragments are read from LDS two ahead of
     // their MFMAs (a rolling three-fragment window), so the read latency
-    // hides behind the previous fragments' MFMAs.
+    // hides behind the previous fragments' MFMAs.  The next step's copies
+    // go out one per token fragment, between its MFMAs: issued together
+    // right after the barrier, as every wave of the CU does at once, they
+    // queue behind each other and hold the wave's MFMAs back.
     constexpr int NI = 4 * FM;
+    static_assert(NCP <= NI, "one copy per token fragment at most");
     auto ldb = [&](int i) {
       const int q = i / FM, fm = i % FM;
       return *reinterpret_cast<const half8*>(cur + 1024 * (4 * fm + g) + 256 * q + 16 * r16);
@@ -579,16 +586,25 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
 #pragma unroll
       for (int f = 0; f < kUnitFrags; ++f)
         acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bb[i % 3], acc[f][fm], 0, 0, 0);
+      if (i < NCP) tiled_copy_one(a16, coff[i] + 256 * sn, nxt, wave + kTiledWaves * i);
     }
     // Pin the order for the scheduler: the two first reads, then per
-    // fragment one read two ahead and its four MFMAs (dequantization VALU
-    // is placed freely between them).
+    // fragment one read two ahead and its four MFMAs with one copy in the
+    // middle (dequantization VALU is placed freely between them).
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (i + 2 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      if (i < NCP) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (copy)
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
     }
+  } else {
+    tiled_copy_step<NCP>(a16, coff, nxt, sn, wave);
   }
   __builtin_amdgcn_sched_barrier(0);
   load_unit_step(w, rec + static_cast<int64_t>(min(s + 2, S - 1)) * kRecBytes, lane);
