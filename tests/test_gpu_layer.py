@@ -129,8 +129,9 @@ def test_layer3_prefill_sampled():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("T", [1, 7, 2048])
+@pytest.mark.parametrize("T", [1, 7, 2048, 8192])
 def test_layer5_large(T):
+    """T = 8192 is the workspace ceiling (the largest forward it accepts)."""
     L = synth.LAYERS[5]
     print(f"layer 5 T={T} (ceiling {L.max_tokens})", flush=True)
     x, logits = synth.activations(5, T), synth.router_logits(5, T)
