@@ -20,6 +20,8 @@
 // lane holds 16 bytes (32 codes) of one weight row; the four MFMAs of the step
 // use its 8-code pieces q = 0..3, and the token operand uses the same k
 // assignment (lane group g holds k = 32g + 8q + i), so every k is summed once.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -113,6 +115,12 @@ __device__ __forceinline__ void g1_store_band_amax(const FwdParams& p, float (*s
     p.act_amax[static_cast<int64_t>(row0 + m) * nbands + band] = v;
   }
 }
+
+// Atomic finalize: GEMM2 results are staged in LDS, 64 columns per row at
+// this pitch (64 + 4 floats: consecutive rows start on different banks), and
+// added into out_acc a row at a time (256 contiguous bytes per atomic
+// instruction).
+constexpr int kAtomicPitch = 68;
 
 // Re-quantize 16 consecutive act values of one expanded row with its g2 (same
 // recipe as the token quantizer, on binary32 input).
@@ -458,8 +466,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
         for (int fm = 0; fm < FM; ++fm) s_amax[wave][fm * 16 + r16] = 0.0f;
     }
     g1_store_band_amax<MT>(p, s_amax, row0, nrows, blockIdx.y, gridDim.y);
-  } else if (kp == 0) {
-    g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16, 1.0f / p.w2g[e]);
+  } else if (p.deterministic) {
+    if (kp == 0)
+      g2_epilogue<FM, kUnitFrags>(p, acc, e, row0, nrows, 64 * j, ginv, slots, g, r16, 1.0f / p.w2g[e]);
+  } else {
+    // atomic finalize: stage the unit's rows in the (now free) LDS operand
+    // area, then one atomic instruction per row (see kAtomicPitch)
+    __syncthreads();
+    if (kp == 0) {
+      float* st = reinterpret_cast<float*>(smem) + ui * MT * kAtomicPitch;
+      const float wginv = 1.0f / p.w2g[e];
+      int tok = 0;
+      float wt = 0.0f;
+      if (lane < nrows) {
+        tok = slot_token(p, slot);
+        wt = slot_weight(p, slot);
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const float alpha = ginv[fm] * wginv;
+#pragma unroll
+        for (int f = 0; f < kUnitFrags; ++f) {
+          const f32x4 v = acc[f][fm];
+          *reinterpret_cast<float4*>(st + (fm * 16 + r16) * kAtomicPitch + 16 * f + 4 * g) =
+              make_float4(v[0] * alpha, v[1] * alpha, v[2] * alpha, v[3] * alpha);
+        }
+      }
+      const int H = p.H;
+      for (int m = 0; m < nrows; ++m) {
+        const float v = st[m * kAtomicPitch + lane];
+        const int tm = __shfl(tok, m, kWave);
+        const float wm = __shfl(wt, m, kWave);
+        atomicAdd(p.out_acc + static_cast<int64_t>(tm) * H + 64 * j + lane, wm * v);
+      }
+    }
   }
 }
 
@@ -638,7 +678,6 @@ struct TiledBlock {
 // columns in LDS (the token buffers, free after the K loop) and reads them
 // back a row at a time, so every atomic instruction covers 256 contiguous
 // bytes of one output row.  Called by every wave of the block (barriers).
-constexpr int kAtomicPitch = 68;  // floats per staged row (64 + 4: row starts on different banks)
 template <int FMV>
 __device__ __forceinline__ void tiled_g2_atomic(const FwdParams& p, TiledShared& sh,
                                                 const f32x4 (&acc)[kUnitFrags][FMV], int row0, int nrows,
@@ -877,10 +916,12 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
 
 int stream_lds_bytes(int fm, int K) { return 16 * fm * ((K / 2 + 16) + (K / 16 + 4)); }
 
-static int stream_lds_total(int fm, int ks, int K) {
+static int stream_lds_total(int fm, int ks, int K, bool atomic = false) {
   const int staged = stream_lds_bytes(fm, K);
   const int red = ks > 1 ? 4 * kUnitFrags * fm * 4 * kWave * 4 : 0;
-  return staged > red ? staged : red;
+  // atomic GEMM2 epilogue: each unit's rows at kAtomicPitch floats
+  const int stage = atomic ? (4 / ks) * 16 * fm * kAtomicPitch * 4 : 0;
+  return std::max(staged, std::max(red, stage));
 }
 
 // Waves that split one unit's K range: the smallest of 1, 2, 4 that gives the
@@ -934,7 +975,7 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
   const int nb2 = (p.H / 64) / (4 / KS2);
   // a multiple of 8 tiles keeps every band of a tile on the same XCD
   const int gx = (max_tiles + 7) / 8 * 8;
-  moe_stream_kernel<FM, KS2, 1><<<dim3(gx, nb2), 256, stream_lds_total(FM, KS2, p.I), s>>>(p);
+  moe_stream_kernel<FM, KS2, 1><<<dim3(gx, nb2), 256, stream_lds_total(FM, KS2, p.I, !p.deterministic), s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
 }
 
