@@ -671,30 +671,32 @@ struct TiledBlock {
   const uint8_t* rec;  // this wave's unit records
 };
 
-// GEMM2 epilogue of the atomic finalize, tiled path: w * y of each row is
-// added into out_acc with fp32 atomics.  The accumulator layout gives each
-// lane 4 columns of 16 rows, so direct atomics would touch 16 rows x 4
-// column groups per instruction; instead each wave stages 32 rows of its 64
+// GEMM2 epilogue, tiled path.  The accumulator layout gives each lane 4
+// columns of 16 rows, so a direct store or atomic would touch 16 rows x 4
+// column groups per instruction.  Instead each wave stages 32 rows of its 64
 // columns in LDS (the token buffers, free after the K loop) and reads them
-// back a row at a time, so every atomic instruction covers 256 contiguous
-// bytes of one output row.  Called by every wave of the block (barriers).
+// back row-major: a y store then writes 4 whole 256-byte row segments per
+// instruction, an atomic (w * y into out_acc) one whole row segment.
+// Called by every wave of the block (barriers).
 template <int FMV>
-__device__ __forceinline__ void tiled_g2_atomic(const FwdParams& p, TiledShared& sh,
+__device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared& sh,
                                                 const f32x4 (&acc)[kUnitFrags][FMV], int row0, int nrows,
                                                 int n0, const float (&ginv)[FMV], float wginv, bool has_unit,
                                                 int wave, int lane) {
   static_assert(kTiledWaves * 32 * kAtomicPitch * 4 <= sizeof(TiledShared::lds), "staging fits the token buffers");
   const int t = threadIdx.x, g = lane >> 4, r16 = lane & 15;
   wait_vmcnt<0>();  // this wave's last copies have landed
-  // every wave is done with the token buffers; each row's token and weight
-  // replace the copy sources and the (unused) amax partials
+  // every wave is done with the token buffers; for the atomics each row's
+  // token and weight replace the copy sources and the (unused) amax partials
   lds_barrier();
-  if (t < kTiledRows) {
-    const int sl = t < nrows ? sh.slot[t] : 0;
-    sh.src[t] = t < nrows ? slot_token(p, sl) : 0;
-    sh.amax[0][t] = t < nrows ? slot_weight(p, sl) : 0.0f;
+  if (!p.deterministic) {
+    if (t < kTiledRows) {
+      const int sl = t < nrows ? sh.slot[t] : 0;
+      sh.src[t] = t < nrows ? slot_token(p, sl) : 0;
+      sh.amax[0][t] = t < nrows ? slot_weight(p, sl) : 0.0f;
+    }
+    lds_barrier();
   }
-  lds_barrier();
   if (!has_unit) return;
   float* st = reinterpret_cast<float*>(&sh.lds[0][0]) + wave * 32 * kAtomicPitch;
   const int H = p.H;
@@ -714,10 +716,21 @@ __device__ __forceinline__ void tiled_g2_atomic(const FwdParams& p, TiledShared&
       }
     }
     const int nr = min(32, nrows - 16 * r);
-    for (int m = 0; m < nr; ++m) {
-      const int lm = 16 * r + m;
-      const float v = st[m * kAtomicPitch + lane];
-      atomicAdd(p.out_acc + static_cast<int64_t>(sh.src[lm]) * H + n0 + lane, sh.amax[0][lm] * v);
+    if (p.deterministic) {
+      // lane l: row 4 i + l / 16, columns 4 (l % 16) .. + 3
+      for (int i = 0; 4 * i < nr; ++i) {
+        const int m = 4 * i + (lane >> 4);
+        if (m < nr) {
+          const float4 v = *reinterpret_cast<const float4*>(st + m * kAtomicPitch + 4 * (lane & 15));
+          *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(row0 + 16 * r + m) * H + n0 + 4 * (lane & 15)) = v;
+        }
+      }
+    } else {
+      for (int m = 0; m < nr; ++m) {
+        const int lm = 16 * r + m;
+        const float v = st[m * kAtomicPitch + lane];
+        atomicAdd(p.out_acc + static_cast<int64_t>(sh.src[lm]) * H + n0 + lane, sh.amax[0][lm] * v);
+      }
     }
   }
 }
@@ -802,10 +815,8 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
       for (int fm = 0; fm < FMV; ++fm) sh.amax[wave][fm * 16 + r16] = 0.0f;
     }
     g1_store_band_amax<kTiledRows>(p, sh.amax, row0, nrows, b.band, b.nb);
-  } else if (p.deterministic) {
-    if (has_unit) g2_epilogue<FMV, kUnitFrags>(p, acc, b.e, row0, nrows, 64 * j, ginv, slots, g, r16, wginv);
   } else {
-    tiled_g2_atomic<FMV>(p, sh, acc, row0, nrows, 64 * j, ginv, wginv, has_unit, wave, lane);
+    tiled_g2_staged<FMV>(p, sh, acc, row0, nrows, 64 * j, ginv, wginv, has_unit, wave, lane);
   }
 }
 
