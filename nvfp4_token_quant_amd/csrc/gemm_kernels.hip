@@ -522,12 +522,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 // its barrier.
 //
 // Ordering of the copies.  Vector loads complete in issue order.  In step s
-// the block issues the copies of step s + 1 right after its barrier and the
-// weight refill of step s + 2 after its MFMAs, so at the start of step s + 1
-// exactly one refill (kRefillOps instructions) was issued after that step's
-// copies: waiting until at most kRefillOps loads are outstanding covers the
-// copies and nothing newer.  Scheduling barriers keep the compiler from
-// moving loads across these points.
+// each wave issues its copies of step s + 1 among its MFMAs (after the
+// barrier that frees that buffer) and the weight refill of step s + 2 after
+// them, so at the start of step s + 1 exactly one refill (kRefillOps
+// instructions) was issued after that step's copies: waiting until at most
+// kRefillOps loads are outstanding covers the copies and nothing newer.
+// Scheduling barriers keep the compiler from moving loads across these
+// points.  Before the first step the block waits for all of its loads.
 // ---------------------------------------------------------------------------
 constexpr int kTiledWaves = 4;
 constexpr int kTiledThreads = kTiledWaves * kWave;
@@ -535,8 +536,8 @@ constexpr int kTiledRows = 128;  // rows of a tile (8 groups of 16)
 constexpr int kRefillOps = kUnitFrags + 1;  // vector memory instructions of load_unit_step
 
 // Rows of the token operand for local row m of a tile: GEMM1 reads the
-// per-token quantized activations of token perm[row] / k, GEMM2 the
-// re-quantized activation of the expanded row itself.
+// per-token quantized activations of the row's token (slot_token), GEMM2
+// the re-quantized activation of the expanded row itself.
 template <int MODE>
 __device__ __forceinline__ void tile_rows(const FwdParams& p, int row0, int nrows, int mt,
                                           int* s_src, float* s_ginv, int* s_slot) {
