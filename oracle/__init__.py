@@ -61,10 +61,12 @@ def _declare(L):
     L.orc_moe_layer.restype = ctypes.c_int
     _F = ctypes.c_float
     L.orc_moe_layer.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64,
-                                _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _P, _P]
+                                _P, _P, _P, _P, _P, _P, _F, _F, ctypes.c_int, _P, _P, _P, _P, _P, _P]
     L.orc_moe_layer_dense.restype = None
     L.orc_moe_layer_dense.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
-                                      _P, _P, _P, _P, _P, _P, _F, _F, _P]
+                                      _P, _P, _P, _P, _P, _P, _F, _F, ctypes.c_int, _P]
+    L.orc_f32_to_bf16.restype = None
+    L.orc_f32_to_bf16.argtypes = [_P, _I64, _P]
     L.orc_philox4x64_10.restype = None
     L.orc_philox4x64_10.argtypes = [_P, _P, _P]
     L.orc_synth_scale.restype = ctypes.c_float
@@ -193,12 +195,16 @@ class QuantWeights:
         self.w2c, self.w2s, self.w2g = _c(w2c, np.uint8), _c(w2s, np.uint8), _c(w2g, np.float32)
 
 
-def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, static_scales=None):
+def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, static_scales=None,
+              a16=False):
     """Layer output (float64 [n_tok, H]) for the listed tokens.
 
     x_bf16: uint16 [T, H]; ids int32 [T, k]; w float64 [T, k] (from router()).
     static_scales: None (per-row global scales) or (g_x, g_a), the static
     global scales of x and of the GEMM2 input.
+    a16: W4A16 — x itself (bf16) and the SwiGLU output rounded to bf16
+    (round to nearest even) are the GEMM inputs; the activations are not
+    quantized (the debug c2 / S2 / g2 are then not written).
     With debug=True also returns a dict of per-slot intermediates.
     """
     gx, ga = (0.0, 0.0) if static_scales is None else static_scales
@@ -217,7 +223,7 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, stati
     rc = lib().orc_moe_layer(
         _p(x_bf16), _p(ids), _p(w), _p(tokens), n, H, I, k, _p(qw.experts), qw.experts.size,
         _p(qw.w13c), _p(qw.w13s), _p(qw.w13g), _p(qw.w2c), _p(qw.w2s), _p(qw.w2g),
-        float(np.float32(gx)), float(np.float32(ga)), _p(out),
+        float(np.float32(gx)), float(np.float32(ga)), int(bool(a16)), _p(out),
         _p(dbg["y"]) if debug else None, _p(dbg["act"]) if debug else None,
         _p(dbg["c2"]) if debug else None, _p(dbg["S2"]) if debug else None,
         _p(dbg["g2"]) if debug else None)
@@ -227,7 +233,7 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, stati
 
 
 def moe_layer_shared(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, shared: QuantWeights,
-                     strategy="sum", static_scales=None):
+                     strategy="sum", static_scales=None, a16=False):
     """Routed output plus a shared expert's output for the listed tokens.
 
     [P3] Command-A-Plus multi-stream page, Cohere2MoeSparseMoeBlock.forward:
@@ -245,15 +251,17 @@ def moe_layer_shared(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, shared: Qua
     if shared.experts.size != 1:
         raise ValueError("shared holds exactly one expert")
     x_bf16 = _c(x_bf16, np.uint16)
-    routed = moe_layer(x_bf16, ids, w, tokens, H, I, qw, static_scales=static_scales)
+    routed = moe_layer(x_bf16, ids, w, tokens, H, I, qw, static_scales=static_scales, a16=a16)
     T = x_bf16.shape[0]
     ids_s = np.full((T, 1), shared.experts[0], np.int32)
     w_s = np.ones((T, 1), np.float64)
-    out = routed + moe_layer(x_bf16, ids_s, w_s, tokens, H, I, shared, static_scales=static_scales)
+    out = routed + moe_layer(x_bf16, ids_s, w_s, tokens, H, I, shared, static_scales=static_scales,
+                             a16=a16)
     return out / 2 if strategy == "average" else out
 
 
-def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g, static_scales=None):
+def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g, static_scales=None,
+                    a16=False):
     x_bf16 = _c(x_bf16, np.uint16)
     ids = _c(ids, np.int32)
     w = _c(w, np.float64)
@@ -264,7 +272,15 @@ def moe_layer_dense(x_bf16, ids, w, H, I, E, w13c, w13s, w13g, w2c, w2s, w2g, st
     gx, ga = (0.0, 0.0) if static_scales is None else static_scales
     lib().orc_moe_layer_dense(_p(x_bf16), _p(ids), _p(w), T, H, I, E, k,
                               *[_p(a) for a in args], float(np.float32(gx)), float(np.float32(ga)),
-                              _p(out))
+                              int(bool(a16)), _p(out))
+    return out
+
+
+def f32_to_bf16(x):
+    """binary32 -> bfloat16 bits (uint16), round to nearest even."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16(_p(x), x.size, _p(out))
     return out
 
 

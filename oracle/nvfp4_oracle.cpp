@@ -50,6 +50,22 @@ float bits_to_float(uint32_t u) {
 // bf16 -> binary32 is exact: the bf16 pattern is the top half of the float.
 float bf16_to_float(uint16_t b) { return bits_to_float(static_cast<uint32_t>(b) << 16); }
 
+// binary32 -> bfloat16 rounded to nearest, ties to even: bf16 keeps the top
+// 16 bits of the binary32 pattern (sign, the 8 exponent bits, 7 fraction
+// bits); the dropped 16 bits decide the rounding (above half: up; exactly
+// half: up only if the kept part is odd).  A carry out of the fraction steps
+// the exponent, which is the correctly rounded result (up to infinity).
+// NaN stays NaN.
+uint16_t float_to_bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  const uint32_t dropped = u & 0xffffu;
+  uint32_t kept = u >> 16;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) ++kept;
+  return static_cast<uint16_t>(kept);
+}
+
 // [MX] E2M1 magnitudes, indexed by the 3 low code bits (e1 e0 m).
 const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
@@ -347,9 +363,11 @@ double silu(double z) { return z / (1.0 + std::exp(-z)); }
 
 // One expert applied to one dequantized activation row xh[H] -> y[H]; also
 // returns the intermediates for the debug entry point.
+// a16: W4A16 (the GEMM2 input is act rounded to bf16 instead of its NVFP4
+// re-quantization; c2, S2, g2 are left untouched).
 void expert_row(const LayerArgs& a, const double* W13, const double* W2, const double* xh,
                 double* h, float* a32, uint8_t* c2, uint8_t* S2, float* g2, double* ah,
-                double* y, float static_ga) {
+                double* y, float static_ga, bool a16) {
   const int64_t H = a.H, I = a.I;
   for (int64_t n = 0; n < 2 * I; ++n) {
     double acc = 0.0;
@@ -357,9 +375,13 @@ void expert_row(const LayerArgs& a, const double* W13, const double* W2, const d
     h[n] = acc;
   }
   for (int64_t i = 0; i < I; ++i) a32[i] = static_cast<float>(silu(h[i]) * h[I + i]);
-  *g2 = static_ga > 0.0f ? static_ga : orc_global_scale(a32, I);
-  quantize_with_g(a32, I, *g2, c2, S2);
-  dequant_rows(c2, S2, *g2, 1, I, ah);
+  if (a16) {
+    for (int64_t i = 0; i < I; ++i) ah[i] = bf16_to_float(float_to_bf16_rne(a32[i]));
+  } else {
+    *g2 = static_ga > 0.0f ? static_ga : orc_global_scale(a32, I);
+    quantize_with_g(a32, I, *g2, c2, S2);
+    dequant_rows(c2, S2, *g2, 1, I, ah);
+  }
   for (int64_t n = 0; n < H; ++n) {
     double acc = 0.0;
     for (int64_t i = 0; i < I; ++i) acc += ah[i] * W2[n * I + i];
@@ -378,6 +400,8 @@ void expert_row(const LayerArgs& a, const double* W13, const double* W2, const d
 //   out      [n_tok, H] binary64
 //   static_gx, static_ga  > 0: static global scales of x and of the GEMM2
 //                         input; <= 0: per-row scales (the default)
+//   a16      1: W4A16 — x (bf16) and act rounded to bf16 are the GEMM
+//            inputs, no activation quantization (c2/S2/g2 debug not written)
 // Optional debug outputs (may be null), per listed token and slot:
 //   y_dbg [n_tok, k, H], act_dbg [n_tok, k, I] (binary32),
 //   c2_dbg [n_tok, k, I/2], S2_dbg [n_tok, k, I/16], g2_dbg [n_tok, k]
@@ -387,7 +411,7 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
                           const int32_t* experts, int64_t n_experts, const uint8_t* w13c,
                           const uint8_t* w13s, const float* w13g, const uint8_t* w2c,
                           const uint8_t* w2s, const float* w2g, float static_gx, float static_ga,
-                          double* out, double* y_dbg, float* act_dbg, uint8_t* c2_dbg,
+                          int a16, double* out, double* y_dbg, float* act_dbg, uint8_t* c2_dbg,
                           uint8_t* S2_dbg, float* g2_dbg) {
   LayerArgs a{H, I, k, w13c, w13s, w2c, w2s, w13g, w2g};
   int32_t max_e = 0;
@@ -400,7 +424,7 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
       if (e > max_e || slot_of[e] < 0) return -1;
     }
 
-  // Activation rows: Q then dequantize (binary64).
+  // Activation rows: Q then dequantize (binary64); W4A16: the bf16 values.
   std::vector<double> xh(static_cast<size_t>(n_tok * H));
   {
     std::vector<uint8_t> c(H / 2), s(H / 16);
@@ -408,6 +432,10 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
     for (int64_t ti = 0; ti < n_tok; ++ti) {
       const uint16_t* xr = x_bf16 + tokens[ti] * H;
       for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(xr[kk]);
+      if (a16) {
+        for (int64_t kk = 0; kk < H; ++kk) xh[ti * H + kk] = xf[kk];
+        continue;
+      }
       float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
       quantize_with_g(xf.data(), H, g, c.data(), s.data());
       dequant_rows(c.data(), s.data(), g, 1, H, xh.data() + ti * H);
@@ -436,7 +464,7 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
         if (ids[tokens[ti] * k + j] != experts[ei]) continue;
         double* y = ybuf.data() + (ti * k + j) * H;
         expert_row(a, W13.data(), W2.data(), xh.data() + ti * H, h.data(), a32.data(), c2.data(),
-                   S2.data(), g2.data(), ah.data(), y, static_ga);
+                   S2.data(), g2.data(), ah.data(), y, static_ga, a16 != 0);
         int64_t slot = ti * k + j;
         if (act_dbg) std::memcpy(act_dbg + slot * I, a32.data(), I * sizeof(float));
         if (c2_dbg) std::memcpy(c2_dbg + slot * (I / 2), c2.data(), I / 2);
@@ -468,7 +496,7 @@ ORC_API void orc_moe_layer_dense(const uint16_t* x_bf16, const int32_t* ids, con
                                  int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  const uint8_t* w13c, const uint8_t* w13s, const float* w13g,
                                  const uint8_t* w2c, const uint8_t* w2s, const float* w2g,
-                                 float static_gx, float static_ga, double* out) {
+                                 float static_gx, float static_ga, int a16, double* out) {
   LayerArgs a{H, I, k, w13c, w13s, w2c, w2s, w13g, w2g};
   std::vector<double> W13(static_cast<size_t>(2 * I * H)), W2(static_cast<size_t>(H * I));
   std::vector<double> xh(H), h(2 * I), ah(I), y(H);
@@ -481,11 +509,15 @@ ORC_API void orc_moe_layer_dense(const uint16_t* x_bf16, const int32_t* ids, con
     dequant_rows(w2c + e * H * (I / 2), w2s + e * H * (I / 16), w2g[e], H, I, W2.data());
     for (int64_t t = 0; t < T; ++t) {
       for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(x_bf16[t * H + kk]);
-      float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
-      quantize_with_g(xf.data(), H, g, c.data(), s.data());
-      dequant_rows(c.data(), s.data(), g, 1, H, xh.data());
+      if (a16) {
+        for (int64_t kk = 0; kk < H; ++kk) xh[kk] = xf[kk];
+      } else {
+        float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
+        quantize_with_g(xf.data(), H, g, c.data(), s.data());
+        dequant_rows(c.data(), s.data(), g, 1, H, xh.data());
+      }
       expert_row(a, W13.data(), W2.data(), xh.data(), h.data(), a32.data(), c2.data(),
-                 S2.data(), g2.data(), ah.data(), y.data(), static_ga);
+                 S2.data(), g2.data(), ah.data(), y.data(), static_ga, a16 != 0);
       double wt = 0.0;
       for (int64_t j = 0; j < k; ++j)
         if (ids[t * k + j] == e) wt = w[t * k + j];
@@ -506,6 +538,11 @@ ORC_API void orc_moe_layer_dense(const uint16_t* x_bf16, const int32_t* ids, con
 // the key is bumped by the Weyl constants W0 = 0x9E3779B97F4A7C15,
 // W1 = 0xBB67AE8584CAA73B between rounds.
 // ---------------------------------------------------------------------------
+// binary32 -> bfloat16 bits, round to nearest even, for n values.
+ORC_API void orc_f32_to_bf16(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_rne(x[i]);
+}
+
 ORC_API void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2],
                                uint64_t out[4]) {
   uint64_t x0 = ctr_in[0], x1 = ctr_in[1], x2 = ctr_in[2], x3 = ctr_in[3];
