@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--shared", choices=["sum", "average"], default=None,
                     help="add a shared expert (weights of E + 1 experts), combined as routed + shared "
                          "or their average")
+    ap.add_argument("--w4a16", action="store_true",
+                    help="bf16 activations (no activation quantization), NVFP4 weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
@@ -148,7 +150,8 @@ def main():
     max_tokens = max(T, L.max_tokens)
     layers = []
     for w in weights:
-        ly = binding.MoeLayer(max_tokens, H, I, E, k, deterministic=det, shared_expert=args.shared)
+        ly = binding.MoeLayer(max_tokens, H, I, E, k, deterministic=det, shared_expert=args.shared,
+                              w4a16=args.w4a16)
         ly.bind(w)
         layers.append(ly)
     out = torch.empty_like(x)
@@ -243,7 +246,8 @@ def main():
     tokens_per_s = T * args.steps / (t1 - t0)
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
-    workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "")
+    workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "") + \
+        ("_w4a16" if args.w4a16 else "")
     traffic = measured_traffic(workload, T, dominant)
     mfma_bound = layer_flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > layer_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
@@ -279,11 +283,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 + e4m3 block-16 + f32 global) operands, f16 MFMA, f32 accumulate",
+        "dtype": ("bf16 activations, nvfp4 weights, bf16 MFMA, f32 accumulate" if args.w4a16 else
+                  "nvfp4 (e2m1 + e4m3 block-16 + f32 global) operands, f16 MFMA, f32 accumulate"),
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
-                   "shared_expert": args.shared,
+                   "shared_expert": args.shared, "activations": "bf16 (W4A16)" if args.w4a16 else "nvfp4",
                    "weights_rotated": args.rotate,
                    "hip_graph": "one graph holding the timed forwards" if not args.eager else "none (eager)",
                    "parallelism": "none (1 GPU)"},
@@ -408,8 +413,8 @@ def cpu_baseline(args, x_bits, T, H, I, k, E):
 
     def run(toks, qw):
         if shared is None:
-            return oracle.moe_layer(x_bits, ids, w, toks, H, I, qw)
-        return oracle.moe_layer_shared(x_bits, ids, w, toks, H, I, qw, shared, args.shared)
+            return oracle.moe_layer(x_bits, ids, w, toks, H, I, qw, a16=args.w4a16)
+        return oracle.moe_layer_shared(x_bits, ids, w, toks, H, I, qw, shared, args.shared, a16=args.w4a16)
     rng = np.random.default_rng(0)
     n = T
     toks = np.arange(T)

@@ -130,6 +130,15 @@ int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, in
 #define MOE_SHARED_EXPERT 0x4u
 #define MOE_SHARED_AVERAGE 0x8u
 
+/* W4A16: bf16 activations, NVFP4 weights.  The pages only name this variant
+ * ([P3] "Related work": a CuTe DSL NVFP4 W4A16 mode); read here as: no
+ * activation is quantized — x itself (bf16) is GEMM1's input and the SwiGLU
+ * output rounded to bf16 (nearest even) is GEMM2's input; the weights stay
+ * NVFP4 (dequantized exactly to bf16 for bf16 MFMA), the outputs are scaled
+ * by 1 / g_w only.  Every batch size runs the tiled GEMMs.  Not combinable
+ * with MOE_STATIC_ACT_SCALES (NVFP4_ERR_INVALID_ARG). */
+#define MOE_W4A16 0x10u
+
 typedef struct moe_config {
   int64_t max_num_tokens; /* token ceiling: every buffer is sized from it once */
   int64_t hidden;         /* H: multiple of 128 */
@@ -260,6 +269,9 @@ int moe_token_ceiling(int64_t max_prefill, int64_t piecewise_max, int64_t graph_
  *   MOE_BUF_ACT       f32 [Rt, I]     SwiGLU output per expanded row
  *   MOE_BUF_A2_CODES  u8 [Rt, I/2]    MOE_BUF_A2_SCALES u8 [Rt, I/16]
  *   MOE_BUF_A2_GSCALE f32 [Rt]        re-quantized activation
+ *   MOE_BUF_A2_16     16-bit [Rt, I]  GEMM2's 16-bit input when the tiled
+ *                     GEMMs run: fp16 of the re-quantized act, or (W4A16)
+ *                     act rounded to bf16
  * where Rt = T*k, plus T with MOE_SHARED_EXPERT: rows [0, T*k) are the
  * routed rows in expert order, row T*k + t the shared expert's row of token
  * t.
@@ -279,6 +291,7 @@ typedef enum moe_buffer_id {
   MOE_BUF_A2_CODES,
   MOE_BUF_A2_SCALES,
   MOE_BUF_A2_GSCALE,
+  MOE_BUF_A2_16,
   MOE_BUF_COUNT_
 } moe_buffer_id;
 

@@ -23,13 +23,14 @@ MOE_DETERMINISTIC_FINALIZE = 0x1
 MOE_STATIC_ACT_SCALES = 0x2
 MOE_SHARED_EXPERT = 0x4
 MOE_SHARED_AVERAGE = 0x8
+MOE_W4A16 = 0x10
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARG", 2: "NVFP4_ERR_TOO_MANY_TOKENS",
           3: "NVFP4_ERR_ALIAS", 4: "NVFP4_ERR_NO_WEIGHTS", 5: "NVFP4_ERR_METADATA_CHANGED",
           6: "NVFP4_ERR_HIP", 7: "NVFP4_ERR_OOM"}
 
 BUF = dict(XQ_CODES=0, XQ_SCALES=1, XQ_GSCALE=2, TOPK_IDS=3, TOPK_W=4, COUNTS=5, OFFSETS=6,
-           PERM=7, INV=8, ACT=9, A2_CODES=10, A2_SCALES=11, A2_GSCALE=12)
+           PERM=7, INV=8, ACT=9, A2_CODES=10, A2_SCALES=11, A2_GSCALE=12, A2_16=13)
 
 
 class Nvfp4Error(RuntimeError):
@@ -233,15 +234,17 @@ class MoeLayer:
     """Workspace + bound weights.  forward(x, logits) -> bf16 [T, H]."""
 
     def __init__(self, max_num_tokens, hidden, inter, num_experts, top_k, deterministic=True,
-                 stream=None, static_act_scales=False, shared_expert=None):
+                 stream=None, static_act_scales=False, shared_expert=None, w4a16=False):
         """shared_expert: None, "sum" or "average" (the weights then hold
-        num_experts + 1 experts, the last one shared by every token)."""
+        num_experts + 1 experts, the last one shared by every token).
+        w4a16: bf16 activations (no activation quantization), NVFP4 weights."""
         if shared_expert not in (None, "sum", "average"):
             raise ValueError("shared_expert must be None, 'sum' or 'average'")
         flags = (MOE_DETERMINISTIC_FINALIZE if deterministic else 0) | \
             (MOE_STATIC_ACT_SCALES if static_act_scales else 0) | \
             (MOE_SHARED_EXPERT if shared_expert else 0) | \
-            (MOE_SHARED_AVERAGE if shared_expert == "average" else 0)
+            (MOE_SHARED_AVERAGE if shared_expert == "average" else 0) | \
+            (MOE_W4A16 if w4a16 else 0)
         self.cfg = MoeConfig(max_num_tokens, hidden, inter, num_experts, top_k, flags)
         h = ctypes.c_void_p()
         _check(lib().moe_workspace_create(ctypes.byref(self.cfg), _stream(stream), ctypes.byref(h)))

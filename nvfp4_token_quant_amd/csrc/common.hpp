@@ -120,6 +120,34 @@ __device__ __forceinline__ half8 dequant8_f16(uint32_t codes, half2v scale2) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// bf16 operands (W4A16).  E4M3 scale byte -> binary32, exactly: the byte
+// shifted to bits 20.. is the binary32 with the same exponent field (bias
+// 127 instead of 7) and fraction, i.e. the value times 2^-120; scaling by
+// 2^120 is exact (subnormal E4M3 values included).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __uint_as_float((b & 0xffu) << 20) * 0x1p120f;
+}
+// 8 E2M1 codes times their block scale as bf16: code (exact in binary32)
+// times the scale is exact in binary32 (at most 6 significant bits), hence
+// also in bf16 (8 significant bits), so the rounding conversion is exact.
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t codes, float scale) {
+  const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(v0[0] * scale);
+  r[1] = static_cast<__bf16>(v0[1] * scale);
+  r[2] = static_cast<__bf16>(v1[0] * scale);
+  r[3] = static_cast<__bf16>(v1[1] * scale);
+  r[4] = static_cast<__bf16>(v2[0] * scale);
+  r[5] = static_cast<__bf16>(v2[1] * scale);
+  r[6] = static_cast<__bf16>(v3[0] * scale);
+  r[7] = static_cast<__bf16>(v3[1] * scale);
+  return r;
+}
+
 __device__ __forceinline__ half2v e4m3_half2(uint32_t b) {
   _Float16 h = static_cast<_Float16>(e4m3_value(b));  // exact: E4M3 values are fp16 values
   half2v r;

@@ -587,7 +587,7 @@ __device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const
 // One K step: wait for this step's copies, start the next step's, MFMAs on
 // the LDS operand `cur` and the weight record in `w`, then refill `w` with
 // the record two steps ahead.
-template <int FM, int NCP>
+template <int FM, int NCP, bool A16>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
                                            uint8_t* nxt, UnitStep& w, const uint8_t* rec, __amdgpu_buffer_rsrc_t a16,
                                            const int (&coff)[NCP], bool has_unit, int wave, int lane) {
@@ -611,7 +611,8 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
     half8 bb[3];
     bb[0] = ldb(0);
     bb[1] = ldb(1);
-    half8 aq[kUnitFrags];
+    half8 aq[kUnitFrags];    // fp16 weight fragments (NVFP4 activations)
+    bf16x8 aqb[kUnitFrags];  // bf16 weight fragments (W4A16)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = i / FM, fm = i % FM;
@@ -621,12 +622,20 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
         for (int f = 0; f < kUnitFrags; ++f) {
           // scale of this q's 16-element block (q 0-1: first byte, q 2-3: second)
           const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1) + 8 * (q >> 1));
-          aq[f] = dequant8_f16(word_of(w.c[f], q), e4m3_to_half2(w16));
+          if constexpr (A16)
+            aqb[f] = dequant8_bf16(word_of(w.c[f], q), e4m3_to_f32(w16));
+          else
+            aq[f] = dequant8_f16(word_of(w.c[f], q), e4m3_to_half2(w16));
         }
       }
 #pragma unroll
-      for (int f = 0; f < kUnitFrags; ++f)
-        acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bb[i % 3], acc[f][fm], 0, 0, 0);
+      for (int f = 0; f < kUnitFrags; ++f) {
+        if constexpr (A16)
+          acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqb[f], __builtin_bit_cast(bf16x8, bb[i % 3]),
+                                                               acc[f][fm], 0, 0, 0);
+        else
+          acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[f], bb[i % 3], acc[f][fm], 0, 0, 0);
+      }
       if (i < NCP) tiled_copy_one(a16, coff[i] + 256 * sn, nxt, wave + kTiledWaves * i);
     }
     // Pin the order for the scheduler: the two first reads, then per
@@ -740,17 +749,19 @@ __device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared&
 // epilogue cover only those groups, so a tile of few rows costs in
 // proportion to its rows (FMV is the smallest of 1, 2, 3, 4, 6, 8 groups
 // that holds them).
-template <int FMV, int MODE>
+template <int FMV, int MODE, bool A16>
 __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, const TiledBlock& b,
                                            UnitStep (&wb)[2], float my_g, int my_slot, float wg) {
   constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
   const int row0 = b.row0, nrows = b.nrows, K = b.K, S = b.S, j = b.j;
   const bool has_unit = b.has_unit;
   const uint8_t* rec = b.rec;
-  // token operand: GEMM1 gathers rows of xq16 [T, K]; GEMM2 reads the tile's
-  // own rows of a2q16 [R, K] (offsets relative to the tile's first row)
+  // token operand: GEMM1 gathers rows of xq16 [T, K] (W4A16: of x itself);
+  // GEMM2 reads the tile's own rows of a2q16 [Rt, K] (offsets relative to
+  // the tile's first row)
+  const _Float16* x16 = A16 ? reinterpret_cast<const _Float16*>(p.x) : p.xq16;
   const __amdgpu_buffer_rsrc_t a16 =
-      MODE == 0 ? tiled_rsrc(p.xq16, static_cast<int64_t>(p.T) * K)
+      MODE == 0 ? tiled_rsrc(x16, static_cast<int64_t>(p.T) * K)
                 : tiled_rsrc(p.a2q16 + static_cast<int64_t>(row0) * K, static_cast<int64_t>(nrows) * K);
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = t & (kWave - 1);
@@ -795,10 +806,10 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   // so that every wait above counts the same loads on every path
   int s = 0;
   for (; s + 1 < S; s += 2) {
-    tiled_step<FMV, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
-    tiled_step<FMV, NCP>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP, A16>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP, A16>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
   }
-  if (s < S) tiled_step<FMV, NCP>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+  if (s < S) tiled_step<FMV, NCP, A16>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
 
   float ginv[FMV];
   int slots[FMV];
@@ -821,7 +832,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   }
 }
 
-template <int MODE>
+template <int MODE, bool A16>
 __global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moe_tiled_kernel(FwdParams p) {
   __shared__ TiledShared sh;
@@ -864,33 +875,51 @@ void moe_tiled_kernel(FwdParams p) {
   load_unit_step(wb[1], b.rec + static_cast<int64_t>(min(1, b.S - 1)) * kRecBytes, lane);
   float my_g = 1.0f;
   int my_slot = -1;
+  // (W4A16: the activations carry no global scale)
   if (MODE == 0) {
     int src = -1;
     if (t < b.nrows) {
       my_slot = row_slot(p, b.row0 + t);
       src = slot_token(p, my_slot);
-      my_g = p.xq_g[src];
+      if (!A16) my_g = p.xq_g[src];
     }
     if (t < kTiledRows) sh.src[t] = src;
     lds_barrier();
   } else if (t < b.nrows) {
-    my_g = p.a2_g[b.row0 + t];
+    if (!A16) my_g = p.a2_g[b.row0 + t];
     my_slot = row_slot(p, b.row0 + t);
   }
   const float wg = MODE == 0 ? p.w13g[b.e] : p.w2g[b.e];
   const int groups = (b.nrows + 15) >> 4;
   if (groups > 6)
-    tiled_tile<8, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<8, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 4)
-    tiled_tile<6, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<6, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 3)
-    tiled_tile<4, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<4, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 2)
-    tiled_tile<3, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<3, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
   else if (groups > 1)
-    tiled_tile<2, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<2, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
   else
-    tiled_tile<1, MODE>(p, sh, b, wb, my_g, my_slot, wg);
+    tiled_tile<1, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
+}
+
+// ---------------------------------------------------------------------------
+// W4A16: GEMM2's input is act rounded to bf16 (nearest even), 8 values per
+// thread into the 16-bit operand buffer the tiled GEMM2 reads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void moe_act_bf16_kernel(FwdParams p) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i >= static_cast<int64_t>(p.Rt) * p.I) return;
+  const float4* src = reinterpret_cast<const float4*>(p.act + i);
+  const float4 a = src[0], b = src[1];
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(a.x); r[1] = static_cast<__bf16>(a.y);
+  r[2] = static_cast<__bf16>(a.z); r[3] = static_cast<__bf16>(a.w);
+  r[4] = static_cast<__bf16>(b.x); r[5] = static_cast<__bf16>(b.y);
+  r[6] = static_cast<__bf16>(b.z); r[7] = static_cast<__bf16>(b.w);
+  *reinterpret_cast<bf16x8*>(p.a2q16 + i) = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -954,7 +983,12 @@ void choose_gemm(int64_t T, FwdParams* p) {
   const int64_t active = R < E ? R : E;
   const int64_t avg = (R + active - 1) / (active > 0 ? active : 1);
   const int Kmax = H > I ? H : I;
-  if (avg <= 16 && stream_lds_total(1, 4, Kmax) <= 65536) {
+  if (p->a16) {
+    // W4A16: the stream kernels stage FP4 token operands; bf16 activations
+    // always take the tiled GEMMs (their 16-bit LDS copies)
+    p->mt = kTiledRows;
+    p->gemm_kind = kGemmTiled;
+  } else if (avg <= 16 && stream_lds_total(1, 4, Kmax) <= 65536) {
     p->mt = 16;
     p->gemm_kind = kGemmStream;
   } else if (avg <= 32 && stream_lds_total(2, 4, Kmax) <= 65536) {
@@ -1018,10 +1052,18 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     // a multiple of 8 tiles keeps every band of a tile on the same XCD (its
     // token rows are then fetched into one L2)
     const int gx = (max_tiles + 7) / 8 * 8;  // == p.tiled_gx
-    moe_tiled_kernel<0><<<gx * nb1, kTiledThreads, 0, s>>>(p);
-    if (ev) (void)hipEventRecord(ev[2], s);
-    moe_requant_kernel<<<(p.Rt + 3) / 4, 256, 0, s>>>(p);
-    moe_tiled_kernel<1><<<gx * nb2, kTiledThreads, 0, s>>>(p);
+    if (p.a16) {
+      moe_tiled_kernel<0, true><<<gx * nb1, kTiledThreads, 0, s>>>(p);
+      if (ev) (void)hipEventRecord(ev[2], s);
+      const int64_t n8 = static_cast<int64_t>(p.Rt) * p.I / 8;
+      moe_act_bf16_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, s>>>(p);
+      moe_tiled_kernel<1, true><<<gx * nb2, kTiledThreads, 0, s>>>(p);
+    } else {
+      moe_tiled_kernel<0, false><<<gx * nb1, kTiledThreads, 0, s>>>(p);
+      if (ev) (void)hipEventRecord(ev[2], s);
+      moe_requant_kernel<<<(p.Rt + 3) / 4, 256, 0, s>>>(p);
+      moe_tiled_kernel<1, false><<<gx * nb2, kTiledThreads, 0, s>>>(p);
+    }
     if (ev) (void)hipEventRecord(ev[3], s);
   }
   return hipGetLastError();

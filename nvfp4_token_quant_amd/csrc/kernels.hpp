@@ -66,6 +66,7 @@ struct FwdParams {
   int g1_bands;       // GEMM1 column bands (partial row amaxes per expanded row)
   int tiled_gx;       // tiled kernels: tile slots of the grid (max tiles rounded up to 8)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
+  int a16;            // 1: W4A16 (x and act as bf16 GEMM inputs, no activation quantization)
   const float* static_g;  // NULL, or [2] static global scales of x and of GEMM2's input
   // caller tensors
   const uint16_t* x;
@@ -94,6 +95,7 @@ struct FwdParams {
   uint8_t* a2_scales;
   float* a2_g;
   _Float16* a2q16;  // [Rt, I] dequantized re-quantized act (exact in fp16); tiled path only
+                    // (W4A16: act rounded to bf16, the same 16-bit slots)
   float* y;        // [Rt, H] (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
   // weights: unit records (see kRecBytes) and per-expert global scales

@@ -269,8 +269,10 @@ int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** ou
   if (c.top_k < 1 || c.top_k > nvfp4::kMaxTopK || c.top_k > c.num_experts)
     return fail(NVFP4_ERR_INVALID_ARG, "top_k must be in [1, min(%d, num_experts)]", nvfp4::kMaxTopK);
   if ((c.flags & ~(MOE_DETERMINISTIC_FINALIZE | MOE_STATIC_ACT_SCALES | MOE_SHARED_EXPERT |
-                   MOE_SHARED_AVERAGE)) != 0)
+                   MOE_SHARED_AVERAGE | MOE_W4A16)) != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "unknown flags 0x%x", c.flags);
+  if ((c.flags & MOE_W4A16) && (c.flags & MOE_STATIC_ACT_SCALES))
+    return fail(NVFP4_ERR_INVALID_ARG, "MOE_W4A16 quantizes no activations: MOE_STATIC_ACT_SCALES does not apply");
   if ((c.flags & MOE_SHARED_AVERAGE) && !(c.flags & MOE_SHARED_EXPERT))
     return fail(NVFP4_ERR_INVALID_ARG, "MOE_SHARED_AVERAGE requires MOE_SHARED_EXPERT");
   if (c.num_experts + ((c.flags & MOE_SHARED_EXPERT) ? 1 : 0) > nvfp4::kMaxExperts)
@@ -391,6 +393,7 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.shared = has_shared(c) ? 1 : 0;
   p.Rt = p.R + (p.shared ? p.T : 0);
   p.combine = (c.flags & MOE_SHARED_AVERAGE) ? 0.5f : 1.0f;
+  p.a16 = (c.flags & MOE_W4A16) ? 1 : 0;
   nvfp4::choose_gemm(T, &p);
   p.deterministic = (c.flags & MOE_DETERMINISTIC_FINALIZE) ? 1 : 0;
   p.static_g = static_scales ? ws->act_scales : nullptr;
@@ -401,7 +404,8 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.xq_scales = ws->xq_scales;
   p.xq_g = ws->xq_g;
   // the fp16 copies are only written and read by the tiled (prefill) kernels
-  p.xq16 = p.gemm_kind == nvfp4::kGemmTiled ? ws->xq16 : nullptr;
+  // (W4A16 reads x itself)
+  p.xq16 = p.gemm_kind == nvfp4::kGemmTiled && !p.a16 ? ws->xq16 : nullptr;
   p.a2q16 = p.gemm_kind == nvfp4::kGemmTiled ? ws->a2q16 : nullptr;
   p.topk_ids = ws->topk_ids;
   p.topk_w = ws->topk_w;
@@ -489,6 +493,7 @@ int moe_workspace_buffer(const moe_workspace* ws, int32_t id, void** ptr_out, in
     case MOE_BUF_A2_CODES: p = ws->a2_codes; n = Rt * I / 2; break;
     case MOE_BUF_A2_SCALES: p = ws->a2_scales; n = Rt * I / 16; break;
     case MOE_BUF_A2_GSCALE: p = ws->a2_g; n = Rt * 4; break;
+    case MOE_BUF_A2_16: p = ws->a2q16; n = Rt * I * 2; break;
     default: return fail(NVFP4_ERR_INVALID_ARG, "unknown buffer id %d", id);
   }
   *ptr_out = p;

@@ -150,8 +150,9 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   const int H = p.H, k = p.k;
   for (int lt = wave; lt < ntok; lt += 4) {
     const int64_t t = t0 + lt;
-    quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
-                          p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
+    if (!p.a16)  // (W4A16 uses x as it is)
+      quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
+                            p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
     route_token_wave<KPL>(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
                           s_ids + lt * k, lane);
     if (!p.deterministic) {
@@ -364,8 +365,9 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   if (blockIdx.x > 0) {
     const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * kSmallWaves + wave;
     if (t < T) {
-      quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
-                            p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
+      if (!p.a16)  // (W4A16 uses x as it is)
+        quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
+                              p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
       if (!p.deterministic) {
         float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
         for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -484,6 +486,13 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
     __shared__ float s_am[kSmallWaves];
     const int q = tid >> 8, qt = tid & 255;  // quarter of the block and thread within it
     const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * 4 + q;
+    if (p.a16) {  // W4A16 uses x as it is: only the atomic accumulator is cleared
+      if (t < T && !p.deterministic) {
+        float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+        for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
     const int nblk = H / 16;
     const uint16_t* xrow = p.x + min(t, static_cast<int64_t>(T - 1)) * H;
     uint4 v[NBL][2];

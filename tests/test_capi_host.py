@@ -58,9 +58,11 @@ def test_workspace_config_checks():
     h = ctypes.c_void_p()
     for cfg in [(0, 2048, 768, 128, 8, 1), (64, 2000, 768, 128, 8, 1), (64, 2048, 700, 128, 8, 1),
                 (64, 2048, 768, 0, 8, 1), (64, 2048, 768, 4, 8, 1), (64, 2048, 768, 128, 17, 1),
-                (64, 2048, 768, 2000, 8, 1), (64, 2048, 768, 128, 8, 0x10),
+                (64, 2048, 768, 2000, 8, 1), (64, 2048, 768, 128, 8, 0x40),
                 # 'average' without a shared expert; no room for the shared expert
-                (64, 2048, 768, 128, 8, 0x9), (64, 2048, 768, 1024, 8, 0x5)]:
+                (64, 2048, 768, 128, 8, 0x9), (64, 2048, 768, 1024, 8, 0x5),
+                # W4A16 quantizes no activations: static scales do not apply
+                (64, 2048, 768, 128, 8, 0x12), (64, 2048, 768, 128, 8, 0x20)]:
         c = binding.MoeConfig(*cfg)
         assert L.moe_workspace_create(ctypes.byref(c), None, ctypes.byref(h)) == 1, cfg
     assert L.moe_workspace_create(None, None, ctypes.byref(h)) == 1
