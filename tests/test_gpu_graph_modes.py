@@ -1,0 +1,48 @@
+"""Captured forwards of the prefill path (tiled GEMMs, the separate
+re-quantization / bf16 conversion kernel) replay bit-identically to eager
+forwards, for the NVFP4 layer, the W4A16 layer and the layer with a shared
+expert; every replay is checked, with eager work and synchronizations between
+the replays."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_token_quant_amd import binding, synth
+from tests.layer_fixtures import gpu_weights, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "w4a16", "shared"])
+def test_tiled_forward_graph_replay(mode):
+    L = synth.LAYERS[1]
+    T = 256
+    print(f"graph replay, layer 1 T={T} mode={mode}", flush=True)
+    shared = "sum" if mode == "shared" else None
+    wts = gpu_weights(1, n_experts=L.E + (1 if shared else 0))
+    layer = binding.MoeLayer(T, L.H, L.I, L.E, L.k, True, shared_expert=shared, w4a16=(mode == "w4a16"))
+    layer.bind(wts)
+    x = to_device_bf16(synth.activations(1, T))
+    logits = torch.from_numpy(synth.router_logits(1, T)).cuda()
+    out = torch.empty_like(x)
+    layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward_into(x, logits, out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    other = torch.empty_like(x)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        layer.forward_into(x[:17], logits[:17], other, T=17)   # eager work between replays
+        torch.cuda.synchronize()
+    layer.close()
