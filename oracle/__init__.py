@@ -62,6 +62,9 @@ def _declare(L):
     _F = ctypes.c_float
     L.orc_moe_layer.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64,
                                 _P, _P, _P, _P, _P, _P, _F, _F, ctypes.c_int, _P, _P, _P, _P, _P, _P]
+    L.orc_moe_layer_xq.restype = ctypes.c_int
+    L.orc_moe_layer_xq.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64,
+                                   _P, _P, _P, _P, _P, _P, _F, _P]
     L.orc_moe_layer_dense.restype = None
     L.orc_moe_layer_dense.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                       _P, _P, _P, _P, _P, _P, _F, _F, ctypes.c_int, _P]
@@ -230,6 +233,37 @@ def moe_layer(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, debug=False, stati
     if rc != 0:
         raise ValueError("a routed expert is missing from the compact weights")
     return (out, dbg) if debug else out
+
+
+def moe_layer_quantized(xq_codes, xq_scales, xq_g, ids, w, tokens, H, I, qw: QuantWeights,
+                        static_ga=None):
+    """Layer output (float64 [n_tok, H]) for activations handed over already
+    quantized: xq_codes u8 [T, H/2], xq_scales u8 [T, H/16] (E4M3 bits),
+    xq_g f32 [T] (encode-direction global scales, value = code x scale / g).
+
+    [P1] "Implementation breakdown" item 2: the runner receives the FP4
+    codes, the block scales and the per-token scale.  The layer's first step
+    (Q of x) is replaced by these rows; the rest is moe_layer's.
+    static_ga: None (per-row re-quantization scales) or the static global
+    scale of the GEMM2 input.
+    """
+    xq_codes = _c(xq_codes, np.uint8)
+    xq_scales = _c(xq_scales, np.uint8)
+    xq_g = _c(xq_g, np.float32).ravel()
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float64)
+    tokens = _c(tokens, np.int64)
+    k = ids.shape[1]
+    n = tokens.size
+    out = np.empty((n, H), np.float64)
+    ga = 0.0 if static_ga is None else float(np.float32(static_ga))
+    rc = lib().orc_moe_layer_xq(
+        _p(xq_codes), _p(xq_scales), _p(xq_g), _p(ids), _p(w), _p(tokens), n, H, I, k,
+        _p(qw.experts), qw.experts.size, _p(qw.w13c), _p(qw.w13s), _p(qw.w13g), _p(qw.w2c),
+        _p(qw.w2s), _p(qw.w2g), ga, _p(out))
+    if rc != 0:
+        raise ValueError("a routed expert is missing from the compact weights")
+    return out
 
 
 def moe_layer_shared(x_bf16, ids, w, tokens, H, I, qw: QuantWeights, shared: QuantWeights,

@@ -391,28 +391,16 @@ void expert_row(const LayerArgs& a, const double* W13, const double* W2, const d
 
 }  // namespace
 
-// Layer output for the tokens listed in `tokens` (n_tok of them).
-//   x_bf16   [T_all, H] activations (bf16 bits); only listed rows are read
-//   ids, w   [T_all, k] routing (from orc_router); only listed rows are read
-//   experts  [n_experts] expert ids present in the compact weight arrays
-//   w13c [n_experts, 2I, H/2], w13s [n_experts, 2I, H/16], w13g [n_experts]
-//   w2c  [n_experts, H, I/2],  w2s  [n_experts, H, I/16],  w2g  [n_experts]
-//   out      [n_tok, H] binary64
-//   static_gx, static_ga  > 0: static global scales of x and of the GEMM2
-//                         input; <= 0: per-row scales (the default)
-//   a16      1: W4A16 — x (bf16) and act rounded to bf16 are the GEMM
-//            inputs, no activation quantization (c2/S2/g2 debug not written)
-// Optional debug outputs (may be null), per listed token and slot:
-//   y_dbg [n_tok, k, H], act_dbg [n_tok, k, I] (binary32),
-//   c2_dbg [n_tok, k, I/2], S2_dbg [n_tok, k, I/16], g2_dbg [n_tok, k]
-// Returns 0, or -1 if a routed expert is missing from `experts`.
-ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const double* w,
-                          const int64_t* tokens, int64_t n_tok, int64_t H, int64_t I, int64_t k,
-                          const int32_t* experts, int64_t n_experts, const uint8_t* w13c,
-                          const uint8_t* w13s, const float* w13g, const uint8_t* w2c,
-                          const uint8_t* w2s, const float* w2g, float static_gx, float static_ga,
-                          int a16, double* out, double* y_dbg, float* act_dbg, uint8_t* c2_dbg,
-                          uint8_t* S2_dbg, float* g2_dbg) {
+namespace {
+
+// The layer from the dequantized activation rows xh [n_tok, H] (binary64) of
+// the listed tokens; the remaining arguments as for orc_moe_layer.
+int layer_from_rows(const std::vector<double>& xh, const int32_t* ids, const double* w,
+                    const int64_t* tokens, int64_t n_tok, int64_t H, int64_t I, int64_t k,
+                    const int32_t* experts, int64_t n_experts, const uint8_t* w13c,
+                    const uint8_t* w13s, const float* w13g, const uint8_t* w2c, const uint8_t* w2s,
+                    const float* w2g, float static_ga, int a16, double* out, double* y_dbg,
+                    float* act_dbg, uint8_t* c2_dbg, uint8_t* S2_dbg, float* g2_dbg) {
   LayerArgs a{H, I, k, w13c, w13s, w2c, w2s, w13g, w2g};
   int32_t max_e = 0;
   for (int64_t i = 0; i < n_experts; ++i) max_e = std::max(max_e, experts[i]);
@@ -423,24 +411,6 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
       int32_t e = ids[tokens[ti] * k + j];
       if (e > max_e || slot_of[e] < 0) return -1;
     }
-
-  // Activation rows: Q then dequantize (binary64); W4A16: the bf16 values.
-  std::vector<double> xh(static_cast<size_t>(n_tok * H));
-  {
-    std::vector<uint8_t> c(H / 2), s(H / 16);
-    std::vector<float> xf(H);
-    for (int64_t ti = 0; ti < n_tok; ++ti) {
-      const uint16_t* xr = x_bf16 + tokens[ti] * H;
-      for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(xr[kk]);
-      if (a16) {
-        for (int64_t kk = 0; kk < H; ++kk) xh[ti * H + kk] = xf[kk];
-        continue;
-      }
-      float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
-      quantize_with_g(xf.data(), H, g, c.data(), s.data());
-      dequant_rows(c.data(), s.data(), g, 1, H, xh.data() + ti * H);
-    }
-  }
 
   std::vector<double> ybuf(static_cast<size_t>(n_tok * k * H));
   // Parallel over experts: each thread dequantizes one expert's weights and
@@ -486,6 +456,72 @@ ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const doub
     }
   if (y_dbg) std::memcpy(y_dbg, ybuf.data(), ybuf.size() * sizeof(double));
   return 0;
+}
+
+}  // namespace
+
+// Layer output for the tokens listed in `tokens` (n_tok of them).
+//   x_bf16   [T_all, H] activations (bf16 bits); only listed rows are read
+//   ids, w   [T_all, k] routing (from orc_router); only listed rows are read
+//   experts  [n_experts] expert ids present in the compact weight arrays
+//   w13c [n_experts, 2I, H/2], w13s [n_experts, 2I, H/16], w13g [n_experts]
+//   w2c  [n_experts, H, I/2],  w2s  [n_experts, H, I/16],  w2g  [n_experts]
+//   out      [n_tok, H] binary64
+//   static_gx, static_ga  > 0: static global scales of x and of the GEMM2
+//                         input; <= 0: per-row scales (the default)
+//   a16      1: W4A16 — x (bf16) and act rounded to bf16 are the GEMM
+//            inputs, no activation quantization (c2/S2/g2 debug not written)
+// Optional debug outputs (may be null), per listed token and slot:
+//   y_dbg [n_tok, k, H], act_dbg [n_tok, k, I] (binary32),
+//   c2_dbg [n_tok, k, I/2], S2_dbg [n_tok, k, I/16], g2_dbg [n_tok, k]
+// Returns 0, or -1 if a routed expert is missing from `experts`.
+ORC_API int orc_moe_layer(const uint16_t* x_bf16, const int32_t* ids, const double* w,
+                          const int64_t* tokens, int64_t n_tok, int64_t H, int64_t I, int64_t k,
+                          const int32_t* experts, int64_t n_experts, const uint8_t* w13c,
+                          const uint8_t* w13s, const float* w13g, const uint8_t* w2c,
+                          const uint8_t* w2s, const float* w2g, float static_gx, float static_ga,
+                          int a16, double* out, double* y_dbg, float* act_dbg, uint8_t* c2_dbg,
+                          uint8_t* S2_dbg, float* g2_dbg) {
+  // Activation rows: Q then dequantize (binary64); W4A16: the bf16 values.
+  std::vector<double> xh(static_cast<size_t>(n_tok * H));
+  std::vector<uint8_t> c(H / 2), s(H / 16);
+  std::vector<float> xf(H);
+  for (int64_t ti = 0; ti < n_tok; ++ti) {
+    const uint16_t* xr = x_bf16 + tokens[ti] * H;
+    for (int64_t kk = 0; kk < H; ++kk) xf[kk] = bf16_to_float(xr[kk]);
+    if (a16) {
+      for (int64_t kk = 0; kk < H; ++kk) xh[ti * H + kk] = xf[kk];
+      continue;
+    }
+    float g = static_gx > 0.0f ? static_gx : orc_global_scale(xf.data(), H);
+    quantize_with_g(xf.data(), H, g, c.data(), s.data());
+    dequant_rows(c.data(), s.data(), g, 1, H, xh.data() + ti * H);
+  }
+  return layer_from_rows(xh, ids, w, tokens, n_tok, H, I, k, experts, n_experts, w13c, w13s, w13g,
+                         w2c, w2s, w2g, static_ga, a16, out, y_dbg, act_dbg, c2_dbg, S2_dbg, g2_dbg);
+}
+
+// The same layer for activations handed over already quantized (the runner
+// contract of [P1] "Implementation breakdown" item 2: FP4 codes, block scales
+// and the per-token global scale go into the expert GEMMs): xq_codes
+// [T_all, H/2], xq_scales [T_all, H/16] (E4M3 bits), xq_g [T_all] (the
+// encode-direction global scale; a value is code x scale / g).  Step 1 of
+// the layer (Q of x) is replaced by these; everything after it is the same.
+ORC_API int orc_moe_layer_xq(const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_g,
+                             const int32_t* ids, const double* w, const int64_t* tokens,
+                             int64_t n_tok, int64_t H, int64_t I, int64_t k, const int32_t* experts,
+                             int64_t n_experts, const uint8_t* w13c, const uint8_t* w13s,
+                             const float* w13g, const uint8_t* w2c, const uint8_t* w2s,
+                             const float* w2g, float static_ga, double* out) {
+  std::vector<double> xh(static_cast<size_t>(n_tok * H));
+  for (int64_t ti = 0; ti < n_tok; ++ti) {
+    const int64_t t = tokens[ti];
+    dequant_rows(xq_codes + t * (H / 2), xq_scales + t * (H / 16), xq_g[t], 1, H,
+                 xh.data() + ti * H);
+  }
+  return layer_from_rows(xh, ids, w, tokens, n_tok, H, I, k, experts, n_experts, w13c, w13s, w13g,
+                         w2c, w2s, w2g, static_ga, 0, out, nullptr, nullptr, nullptr, nullptr,
+                         nullptr);
 }
 
 // Brute-force dense variant (tiny inputs): every expert is applied to every
