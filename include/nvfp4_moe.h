@@ -219,6 +219,33 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
                       void* out_dev, void* stream);
 
 /*
+ * The same forward for activations the caller has already quantized, as the
+ * runner of [P1] "Implementation breakdown" item 2 is handed them (FP4 codes,
+ * block scales and the per-token global scale, consumed by the expert GEMMs
+ * as they are).  Step Q1 is skipped; everything after it is
+ * moe_nvfp4_forward's, so codes that nvfp4_quantize_per_token wrote for x
+ * give exactly moe_nvfp4_forward(x)'s output (bit for bit with
+ * MOE_DETERMINISTIC_FINALIZE).
+ *
+ *   x_codes_dev   u8 [T, H/2], two E2M1 codes per byte (even element in the
+ *                 low nibble), 16-byte aligned
+ *   x_scales_dev  u8 [T, H/16], E4M3 block scales, 16-byte aligned; no NaN
+ *                 byte (0x7F / 0xFF) is checked for: one gives NaN outputs
+ *   x_gscale_dev  f32 [T], encode-direction global scales (a value is
+ *                 code x scale / g), 4-byte aligned, finite and > 0
+ *   logits_dev, T, out_dev, stream   as for moe_nvfp4_forward; out must not
+ *                 overlap the three activation arrays (NVFP4_ERR_ALIAS)
+ * The three arrays are read in place (borrowed for the call's duration on
+ * `stream`) and never written.  With MOE_STATIC_ACT_SCALES only the GEMM2
+ * input scale (scales[1]) is used.  A MOE_W4A16 workspace returns
+ * NVFP4_ERR_INVALID_ARG (it takes bf16 activations).  No allocation and no
+ * host synchronization.
+ */
+int moe_nvfp4_forward_quantized(moe_workspace* ws, const void* x_codes_dev, const void* x_scales_dev,
+                                const float* x_gscale_dev, const float* logits_dev, int64_t T,
+                                void* out_dev, void* stream);
+
+/*
  * Reload after the caller updated the weights in place ([P1]
  * "Implementation breakdown" item 3 and "Source snippets",
  * refresh_cutedsl_standard_scales_for_weight_update): the codes (re-read

@@ -78,6 +78,8 @@ def lib():
         L.moe_workspace_bind_weights.argtypes = [_P, ctypes.POINTER(MoeWeights), _P]
         L.moe_nvfp4_forward.restype = ctypes.c_int
         L.moe_nvfp4_forward.argtypes = [_P, _P, _P, _I64, _P, _P]
+        L.moe_nvfp4_forward_quantized.restype = ctypes.c_int
+        L.moe_nvfp4_forward_quantized.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P]
         L.refresh_scales_inplace.restype = ctypes.c_int
         L.refresh_scales_inplace.argtypes = [_P, ctypes.POINTER(MoeWeights), _P]
         L.moe_workspace_destroy.restype = ctypes.c_int
@@ -281,6 +283,28 @@ class MoeLayer:
         logits = logits.contiguous()
         out = torch.empty_like(x)
         return self.forward_into(x, logits, out, stream=stream)
+
+    def forward_quantized_into(self, codes, scales, gscale, logits, out, T=None, stream=None):
+        T = codes.shape[0] if T is None else T
+        _check(lib().moe_nvfp4_forward_quantized(self.handle, _ptr(codes), _ptr(scales), _ptr(gscale),
+                                                 _ptr(logits), T, _ptr(out), _stream(stream)))
+        return out
+
+    def forward_quantized(self, codes, scales, gscale, logits, stream=None):
+        """The forward for activations already quantized per token: codes
+        uint8 [T, H/2], scales uint8 [T, H/16] (E4M3 bits), gscale float32
+        [T] (as quantize_per_token returns them); bf16 [T, H] out."""
+        _require(codes, torch.uint8, "codes")
+        _require(scales, torch.uint8, "scales")
+        _require(gscale, torch.float32, "gscale")
+        _require(logits, torch.float32, "logits")
+        T = codes.shape[0]
+        H = codes.shape[1] * 2
+        if tuple(scales.shape) != (T, H // 16) or tuple(gscale.shape) != (T,):
+            raise ValueError("scales must be [T, H/16] and gscale [T] for codes [T, H/2]")
+        codes, scales, gscale, logits = (t.contiguous() for t in (codes, scales, gscale, logits))
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=codes.device)
+        return self.forward_quantized_into(codes, scales, gscale, logits, out, stream=stream)
 
     def buffer(self, name: str):
         """(device pointer, bytes) of an intermediate buffer."""

@@ -67,6 +67,8 @@ struct FwdParams {
   int tiled_gx;       // tiled kernels: tile slots of the grid (max tiles rounded up to 8)
   int deterministic;  // 1: slot-ordered finalize; 0: fp32 atomics into out_acc
   int a16;            // 1: W4A16 (x and act as bf16 GEMM inputs, no activation quantization)
+  int preq;           // 1: x handed over already quantized: xq_codes / xq_scales / xq_g are
+                      //    the caller's (read only), x is not read
   const float* static_g;  // NULL, or [2] static global scales of x and of GEMM2's input
   // caller tensors
   const uint16_t* x;

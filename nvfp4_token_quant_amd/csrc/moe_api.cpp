@@ -362,10 +362,22 @@ int moe_workspace_set_act_scales(moe_workspace* ws, const float* scales_dev, voi
   return ok();
 }
 
-int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_dev, int64_t T,
-                      void* out_dev, void* stream) {
+namespace {
+
+// Activations handed over already quantized (codes [T, H/2], scales [T, H/16],
+// global scales [T]); on = false: the forward quantizes x itself.
+struct XQ {
+  bool on;
+  const void* codes;
+  const void* scales;
+  const float* g;
+};
+
+int forward_impl(moe_workspace* ws, const void* x_dev, const XQ& xq, const float* logits_dev, int64_t T,
+                 void* out_dev, void* stream) {
   if (!ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL workspace");
   const moe_config& c = ws->cfg;
+  const bool preq = xq.on;
   if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
   if (T > c.max_num_tokens)
     return fail(NVFP4_ERR_TOO_MANY_TOKENS, "num_tokens (%lld) exceeds max_num_tokens (%lld)",
@@ -374,13 +386,28 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   const bool static_scales = (c.flags & MOE_STATIC_ACT_SCALES) != 0;
   if (static_scales && !ws->act_scales_set)
     return fail(NVFP4_ERR_INVALID_ARG, "static activation scales not set; call moe_workspace_set_act_scales");
+  if (preq && (c.flags & MOE_W4A16))
+    return fail(NVFP4_ERR_INVALID_ARG, "a MOE_W4A16 workspace takes bf16 activations, not quantized ones");
   if (T == 0) return ok();
-  if (!x_dev || !logits_dev || !out_dev) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
-  if (!aligned(x_dev, 16) || !aligned(out_dev, 16) || !aligned(logits_dev, 4))
-    return fail(NVFP4_ERR_INVALID_ARG, "x and out must be 16-byte aligned, logits 4-byte aligned");
   const int64_t H = c.hidden, E = c.num_experts;
-  if (overlap(out_dev, T * H * 2, x_dev, T * H * 2) || overlap(out_dev, T * H * 2, logits_dev, T * E * 4))
-    return fail(NVFP4_ERR_ALIAS, "out overlaps x or the router logits (the layer is not in-place)");
+  if (!logits_dev || !out_dev) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(out_dev, 16) || !aligned(logits_dev, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "out must be 16-byte aligned, logits 4-byte aligned");
+  if (overlap(out_dev, T * H * 2, logits_dev, T * E * 4))
+    return fail(NVFP4_ERR_ALIAS, "out overlaps the router logits (the layer is not in-place)");
+  if (preq) {
+    if (!xq.codes || !xq.scales || !xq.g) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(xq.codes, 16) || !aligned(xq.scales, 16) || !aligned(xq.g, 4))
+      return fail(NVFP4_ERR_INVALID_ARG, "codes and scales must be 16-byte aligned, global scales 4-byte aligned");
+    if (overlap(out_dev, T * H * 2, xq.codes, T * H / 2) || overlap(out_dev, T * H * 2, xq.scales, T * H / 16) ||
+        overlap(out_dev, T * H * 2, xq.g, T * 4))
+      return fail(NVFP4_ERR_ALIAS, "out overlaps the quantized activations (the layer is not in-place)");
+  } else {
+    if (!x_dev) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(x_dev, 16)) return fail(NVFP4_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    if (overlap(out_dev, T * H * 2, x_dev, T * H * 2))
+      return fail(NVFP4_ERR_ALIAS, "out overlaps x (the layer is not in-place)");
+  }
 
   nvfp4::FwdParams p;
   std::memset(&p, 0, sizeof(p));
@@ -400,9 +427,11 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
   p.x = static_cast<const uint16_t*>(x_dev);
   p.logits = logits_dev;
   p.out = static_cast<uint16_t*>(out_dev);
-  p.xq_codes = ws->xq_codes;
-  p.xq_scales = ws->xq_scales;
-  p.xq_g = ws->xq_g;
+  p.preq = preq ? 1 : 0;
+  // handed-over codes are read in place (no kernel writes them when preq)
+  p.xq_codes = preq ? static_cast<uint8_t*>(const_cast<void*>(xq.codes)) : ws->xq_codes;
+  p.xq_scales = preq ? static_cast<uint8_t*>(const_cast<void*>(xq.scales)) : ws->xq_scales;
+  p.xq_g = preq ? const_cast<float*>(xq.g) : ws->xq_g;
   // the fp16 copies are only written and read by the tiled (prefill) kernels
   // (W4A16 reads x itself)
   p.xq16 = p.gemm_kind == nvfp4::kGemmTiled && !p.a16 ? ws->xq16 : nullptr;
@@ -436,6 +465,20 @@ int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_
                                            ws->timing ? ws->events : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_forward launch");
   return ok();
+}
+
+}  // namespace
+
+int moe_nvfp4_forward(moe_workspace* ws, const void* x_dev, const float* logits_dev, int64_t T,
+                      void* out_dev, void* stream) {
+  return forward_impl(ws, x_dev, XQ{false, nullptr, nullptr, nullptr}, logits_dev, T, out_dev, stream);
+}
+
+int moe_nvfp4_forward_quantized(moe_workspace* ws, const void* x_codes_dev, const void* x_scales_dev,
+                                const float* x_gscale_dev, const float* logits_dev, int64_t T, void* out_dev,
+                                void* stream) {
+  return forward_impl(ws, nullptr, XQ{true, x_codes_dev, x_scales_dev, x_gscale_dev}, logits_dev, T, out_dev,
+                      stream);
 }
 
 int moe_workspace_destroy(moe_workspace* ws) {

@@ -150,9 +150,13 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
   const int H = p.H, k = p.k;
   for (int lt = wave; lt < ntok; lt += 4) {
     const int64_t t = t0 + lt;
-    if (!p.a16)  // (W4A16 uses x as it is)
+    if (p.preq) {  // codes handed over: only the tiled GEMMs' fp16 copy is written
+      if (p.xq16) dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H,
+                                  lane, kWave);
+    } else if (!p.a16) {  // (W4A16 uses x as it is)
       quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
                             p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
+    }
     route_token_wave<KPL>(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
                           s_ids + lt * k, lane);
     if (!p.deterministic) {
@@ -365,9 +369,14 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   if (blockIdx.x > 0) {
     const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * kSmallWaves + wave;
     if (t < T) {
-      if (!p.a16)  // (W4A16 uses x as it is)
+      if (p.preq) {  // codes handed over: only the tiled GEMMs' fp16 copy is written
+        if (p.xq16)
+          dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H, lane,
+                          kWave);
+      } else if (!p.a16) {  // (W4A16 uses x as it is)
         quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
                               p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
+      }
       if (!p.deterministic) {
         float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
         for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -486,7 +495,10 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
     __shared__ float s_am[kSmallWaves];
     const int q = tid >> 8, qt = tid & 255;  // quarter of the block and thread within it
     const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * 4 + q;
-    if (p.a16) {  // W4A16 uses x as it is: only the atomic accumulator is cleared
+    if (p.a16 || p.preq) {  // W4A16 uses x as it is; handed-over codes only need the fp16
+                            // copy of the tiled GEMMs (if any) and the atomic accumulator cleared
+      if (t < T && p.preq && p.xq16)
+        dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H, qt, 256);
       if (t < T && !p.deterministic) {
         float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
         for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);

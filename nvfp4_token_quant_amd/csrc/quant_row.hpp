@@ -56,6 +56,17 @@ __device__ __forceinline__ void store_block_f16(_Float16* dst, uint32_t lo, uint
   d[1] = dequant8_f16(hi, sc);
 }
 
+// The fp16 copy of a row handed over already quantized: blocks b0, b0 + step,
+// ... of codes crow / scales srow.
+__device__ __forceinline__ void dequant_row_f16(const uint8_t* __restrict__ crow,
+                                                const uint8_t* __restrict__ srow, int nblk,
+                                                _Float16* __restrict__ x16row, int b0, int step) {
+  for (int b = b0; b < nblk; b += step) {
+    const uint2 c = *reinterpret_cast<const uint2*>(crow + 8 * b);
+    store_block_f16(x16row + 16 * b, c.x, c.y, srow[b]);
+  }
+}
+
 // Row amax -> g, then every block of the row; the block amaxes of the first
 // pass are reused by the second.  gfix: NULL for the row's own global scale
 // 2688 / amax, else a given one.

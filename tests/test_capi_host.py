@@ -68,5 +68,6 @@ def test_workspace_config_checks():
     assert L.moe_workspace_create(None, None, ctypes.byref(h)) == 1
     # calls on a NULL workspace fail before touching the device
     assert L.moe_nvfp4_forward(None, None, None, 1, None, None) == 1
+    assert L.moe_nvfp4_forward_quantized(None, None, None, None, None, 1, None, None) == 1
     assert L.refresh_scales_inplace(None, None, None) == 1
     assert L.moe_workspace_destroy(None) == 0
