@@ -73,6 +73,69 @@ __global__ __launch_bounds__(256) void quantize_rows_block_kernel(const uint16_t
   if (t == 0) gs[row] = g;
 }
 
+// Rows of up to 2048 half-blocks (cols <= 16384): one block of 256 threads per
+// row, thread t owning the 8-element halves t, t + 256, ... (NH of them) of
+// the row's 16-element blocks.  Each wave instruction then reads 1 KB of
+// contiguous row and writes 256 contiguous code bytes; a block's two halves
+// sit in lanes 2i and 2i + 1, which exchange their half amaxes (one lane
+// swap) and both derive the same block scale.  The even lane writes it.
+template <int NH>
+__global__ __launch_bounds__(256) void quantize_rows_pair_kernel(const uint16_t* __restrict__ x,
+                                                                 int64_t rows, int cols, int64_t ld,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ gs) {
+  __shared__ float s_am[4];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int nhalf = cols / 8;
+  const uint16_t* xrow = x + row * ld;
+  uint4 v[NH];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) v[i] = load_stream16(xrow + 8 * min(t + 256 * i, nhalf - 1));
+  // half amaxes (|x| of finite bf16 orders like its low 15 bits), block
+  // amaxes from the partner lane, row amax over the valid halves
+  float bam[NH];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    const float ha = __uint_as_float(m << 16);
+    bam[i] = fmaxf(ha, __shfl_xor(ha, 1, kWave));
+    if (t + 256 * i < nhalf) am = fmaxf(am, ha);
+  }
+  am = wave_max(am);
+  if (lane == 0) s_am[wave] = am;
+  __syncthreads();
+  const float g = global_scale(fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3])));
+  uint8_t* crow = codes + row * (cols / 2);
+  uint8_t* srow = scales + row * (cols / 16);
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int h = t + 256 * i;
+    if (h < nhalf) {
+      const float sg = div6_rn(bam[i] * g);
+      const uint32_t sb = e4m3_encode(sg);
+      const float d = e4m3_value(sb);
+      const float r = d > 0.0f ? div_e4m3_rn(g, d) : 0.0f;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __builtin_amdgcn_fmed3f(bf16_lo(w[j]) * r, -6.0f, 6.0f);
+        f[2 * j + 1] = __builtin_amdgcn_fmed3f(bf16_hi(w[j]) * r, -6.0f, 6.0f);
+      }
+      // streaming stores: the outputs are not re-read by this kernel
+      __builtin_nontemporal_store(e2m1_pack8(f), reinterpret_cast<uint32_t*>(crow + 4 * h));
+      if (!(h & 1)) __builtin_nontemporal_store(static_cast<uint8_t>(sb), srow + h / 2);
+    }
+  }
+  if (t == 0) gs[row] = g;
+}
+
 // Longer rows: one wave per row, two passes over the row.
 __global__ __launch_bounds__(256) void quantize_rows_long_kernel(const uint16_t* __restrict__ x,
                                                                  int64_t rows, int cols, int64_t ld,
@@ -100,6 +163,17 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
   const int64_t nbl = (cols / 16 + 255) / 256;
   const unsigned grid = static_cast<unsigned>(rows);
   const int c = static_cast<int>(cols);
+  switch ((cols / 8 + 255) / 256) {
+    case 1: quantize_rows_pair_kernel<1><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 2: quantize_rows_pair_kernel<2><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 3: quantize_rows_pair_kernel<3><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 4: quantize_rows_pair_kernel<4><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 5: quantize_rows_pair_kernel<5><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 6: quantize_rows_pair_kernel<6><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 7: quantize_rows_pair_kernel<7><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    case 8: quantize_rows_pair_kernel<8><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); return hipGetLastError();
+    default: break;
+  }
   switch (nbl) {
     case 1: quantize_rows_block_kernel<1><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
     case 2: quantize_rows_block_kernel<2><<<grid, 256, 0, s>>>(x, rows, c, ld, codes, scales, gs); break;
