@@ -46,3 +46,38 @@ def test_tiled_forward_graph_replay(mode):
         layer.forward_into(x[:17], logits[:17], other, T=17)   # eager work between replays
         torch.cuda.synchronize()
     layer.close()
+
+
+@pytest.mark.parametrize("T", [64, 256])
+def test_prequantized_forward_graph_replay(T):
+    """The forward on handed-over codes (decode-sized stream path at T = 64,
+    tiled path at T = 256) captured and replayed equals the eager forward on
+    x, whose codes they are."""
+    L = synth.LAYERS[1]
+    print(f"graph replay, layer 1 T={T} pre-quantized", flush=True)
+    layer = binding.MoeLayer(T, L.H, L.I, L.E, L.k, True)
+    layer.bind(gpu_weights(1))
+    x = to_device_bf16(synth.activations(1, T))
+    logits = torch.from_numpy(synth.router_logits(1, T)).cuda()
+    codes, scales, gs = binding.quantize_per_token(x)
+    eager = layer.forward(x, logits)
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward_quantized_into(codes, scales, gs, logits, out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward_quantized_into(codes, scales, gs, logits, out)
+    torch.cuda.synchronize()
+    other = torch.empty_like(x)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+        layer.forward_into(x[:17], logits[:17], other, T=17)   # eager work between replays
+        torch.cuda.synchronize()
+    layer.close()

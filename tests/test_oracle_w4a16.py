@@ -1,6 +1,6 @@
 """Pins of the oracle's W4A16 mode (bf16 activations, NVFP4 weights; the
-variant SURVEY names after the per-token path — the pages only name it, as a
-related PR title on [P3]): x itself (bf16) is GEMM1's input, the SwiGLU
+variant the pages only name, as a related PR title on [P3], read here as
+bf16 activations that skip both activation quantizations): x itself (bf16) is GEMM1's input, the SwiGLU
 output rounded to bf16 (round to nearest, ties to even) is GEMM2's input, the
 weights are dequantized NVFP4 with their per-expert global scales.
 
