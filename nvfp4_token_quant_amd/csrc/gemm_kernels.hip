@@ -311,20 +311,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   if constexpr (MODE == 0) {
     // Source rows of the tile.  The row table load goes first, so that
     // waiting for it does not wait for weights.
-    int src = 0;
-    if (lane < nrows) slot = row_slot(p, row0 + lane);
+    // (lanes past nrows take the last row: the table load and the wait for
+    // it are then on every path, ahead of the copies)
+    slot = row_slot(p, row0 + min(lane, nrows - 1));
 #pragma unroll
     for (int d = 0; d < kStreamEarly; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-    if (lane < nrows) src = slot_token(p, slot);
+    const int src = slot_token(p, slot);
     const int cbytes = K / 2, sbytes = K / 16;
     for (int m = wave; m < nrows; m += 4) {
       const int64_t sm = __builtin_amdgcn_readlane(src, m);
       copy_rows_to_lds<16>(p.xq_codes + sm * cbytes, lc + m * cpitch, cbytes, lane);
       copy_rows_to_lds<4>(p.xq_scales + sm * sbytes, ls + m * spitch, sbytes, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // The rest of the prefetch window goes out behind the copies; vector
+    // memory counts complete in issue order, so waiting until only those
+    // records are outstanding covers the copies (and the first records)
+    // without draining the window.  Each load_unit_step is kUnitFrags + 1
+    // instructions; the records are used on a run-time condition, so none
+    // is dropped, and the scheduling barriers keep the issue order.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = kStreamEarly; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(D - kStreamEarly) * (kUnitFrags + 1)>();
+    __builtin_amdgcn_sched_barrier(0);
     // the epilogue's row scales (used after the loop)
     if (lane < nrows) grow = p.xq_g[src];
   } else {
