@@ -80,6 +80,32 @@ def test_layer_equals_dense_bruteforce():
     assert np.all(np.isfinite(out))
 
 
+def test_layer_and_routing_invariant_under_token_order():
+    """Shuffling the tokens (rows of x and of the logits) shuffles the router
+    output and the layer output the same way, value for value: each token's
+    result depends on that token alone.  The expandInputRows permutation is
+    rebuilt for the new order and stays a stable counting sort (rows of one
+    expert in ascending (token, slot) order), so it is not simply permuted."""
+    L = synth.LAYERS[1]
+    x = synth.activations(1)
+    logits = synth.router_logits(1)
+    _, _, q13, q2 = _tiny_weights()
+    qw = oracle.QuantWeights(np.arange(L.E), *q13, *q2)
+    ids, w = oracle.router(logits, L.k)
+    out = oracle.moe_layer(x, ids, w, np.arange(L.T), L.H, L.I, qw)
+    pi = np.random.default_rng(17).permutation(L.T)
+    ids_p, w_p = oracle.router(logits[pi], L.k)
+    np.testing.assert_array_equal(ids_p, ids[pi])
+    np.testing.assert_array_equal(w_p, w[pi])
+    out_p = oracle.moe_layer(x[pi], ids_p, w_p, np.arange(L.T), L.H, L.I, qw)
+    np.testing.assert_array_equal(out_p, out[pi])
+    counts, offsets, perm, inv = oracle.permute(ids_p, L.E)
+    flat = ids_p.ravel()
+    for e in range(L.E):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[rows] == e) and np.all(np.diff(rows) > 0)
+
+
 def test_layer_intermediates_against_numpy():
     L = synth.LAYERS[1]
     x = synth.activations(1)
