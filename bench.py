@@ -79,6 +79,9 @@ def parse():
                          "or their average")
     ap.add_argument("--w4a16", action="store_true",
                     help="bf16 activations (no activation quantization), NVFP4 weights")
+    ap.add_argument("--prequantized", action="store_true",
+                    help="time the forward on activations already quantized per token (codes, block "
+                         "scales, global scales made once before timing), the runner contract")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
@@ -118,6 +121,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the layer runs on a single MI355X; no collectives are built)", file=sys.stderr)
         sys.exit(2)
+    if args.prequantized and args.w4a16:
+        print("--prequantized applies to NVFP4 activations; --w4a16 takes bf16 ones", file=sys.stderr)
+        sys.exit(2)
     import numpy as np
     import torch
 
@@ -155,10 +161,18 @@ def main():
         ly.bind(w)
         layers.append(ly)
     out = torch.empty_like(x)
+    if args.prequantized:
+        xq = binding.quantize_per_token(x)   # the handed-over activations (outside the timed region)
+
+    def fwd(ly):
+        if args.prequantized:
+            ly.forward_quantized_into(*xq, logits, out)
+        else:
+            ly.forward_into(x, logits, out)
     torch.cuda.synchronize()
 
     # routing statistics for the algorithmic byte / FLOP counts, from the GPU's own counts
-    layers[0].forward_into(x, logits, out)
+    fwd(layers[0])
     torch.cuda.synchronize()
     counts = layers[0].read_buffer("COUNTS", torch.int32, (E,)).cpu().numpy()
     active = int((counts > 0).sum()) + n_shared  # the shared expert counts as one more active expert
@@ -166,20 +180,21 @@ def main():
     w13_bytes = 2 * I * H * 0.5625 + 4
     w2_bytes = H * I * 0.5625 + 4
     stage_bytes = {
-        "prologue": T * H * 2 + T * E * 4 + T * (H * 0.5625 + 4) + T * k * 8,
+        "prologue": (0 if args.prequantized else T * H * 2 + T * (H * 0.5625 + 4)) + T * E * 4 + T * k * 8,
         "gemm1": active * w13_bytes + R * (H * 0.5625 + 4),
         "gemm2": active * w2_bytes,
         "finalize": T * H * 2,
     }
     stage_flops = {"prologue": 0.0, "gemm1": 2.0 * R * 2 * I * H, "gemm2": 2.0 * R * H * I,
                    "finalize": 2.0 * R * H}
-    layer_bytes = active * (w13_bytes + w2_bytes) + T * H * 2 + T * E * 4 + T * H * 2
+    x_bytes = T * (H * 0.5625 + 4) if args.prequantized else T * H * 2
+    layer_bytes = active * (w13_bytes + w2_bytes) + x_bytes + T * E * 4 + T * H * 2
     layer_flops = 6.0 * R * I * H
 
     hip = Hip()
     stages = ["prologue", "gemm1", "gemm2", "finalize"]
     for i in range(args.warmup):
-        layers[i % len(layers)].forward_into(x, logits, out)
+        fwd(layers[i % len(layers)])
     torch.cuda.synchronize()
     lib = binding.lib()
     lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
@@ -200,13 +215,13 @@ def main():
                     lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
                     # record the events once outside the graph (HIP reports no
                     # elapsed time for events only ever recorded by graph nodes)
-                    ly.forward_into(x, logits, out)
+                    fwd(ly)
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     for i, ev in enumerate(ev_sets):
                         ly = layers[(first + i) % len(layers)]
                         lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
-                        ly.forward_into(x, logits, out)
+                        fwd(ly)
             return g
 
         warm_graph = capture(warm_evs, 0)
@@ -229,7 +244,7 @@ def main():
         for i in range(args.steps):
             ly = layers[i % len(layers)]
             lib.moe_workspace_set_stage_events(ly.handle, arrs[i])
-            ly.forward_into(x, logits, out)
+            fwd(ly)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     per_stage = {s: [] for s in stages}
@@ -247,7 +262,7 @@ def main():
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
     workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "") + \
-        ("_w4a16" if args.w4a16 else "")
+        ("_w4a16" if args.w4a16 else "") + ("_prequantized" if args.prequantized else "")
     traffic = measured_traffic(workload, T, dominant)
     mfma_bound = layer_flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > layer_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
@@ -288,7 +303,9 @@ def main():
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
         "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
-                   "shared_expert": args.shared, "activations": "bf16 (W4A16)" if args.w4a16 else "nvfp4",
+                   "shared_expert": args.shared,
+                   "activations": "bf16 (W4A16)" if args.w4a16 else
+                   ("nvfp4, quantized before the forward" if args.prequantized else "nvfp4"),
                    "weights_rotated": args.rotate,
                    "hip_graph": "one graph holding the timed forwards" if not args.eager else "none (eager)",
                    "parallelism": "none (1 GPU)"},
@@ -411,7 +428,11 @@ def cpu_baseline(args, x_bits, T, H, I, k, E):
     if args.shared:
         shared = oracle.QuantWeights(np.array([E], np.int32), *(a[None] for a in oracle_expert(args.layer, E)))
 
+    xq = oracle.quantize_rows(x_bits) if args.prequantized else None
+
     def run(toks, qw):
+        if xq is not None:
+            return oracle.moe_layer_quantized(*xq, ids, w, toks, H, I, qw)
         if shared is None:
             return oracle.moe_layer(x_bits, ids, w, toks, H, I, qw, a16=args.w4a16)
         return oracle.moe_layer_shared(x_bits, ids, w, toks, H, I, qw, shared, args.shared, a16=args.w4a16)

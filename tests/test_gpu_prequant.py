@@ -117,3 +117,40 @@ def test_prequantized_errors_and_empty():
     with pytest.raises(binding.Nvfp4Error):
         layer.forward_quantized_into(codes_in_out, _dev(xs), _dev(xg), logits, buf.view(torch.bfloat16).view(T, L.H))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [64, 1024])
+def test_prequantized_with_shared_expert_and_static_scales(T):
+    """With a shared expert ('average'), and with static activation scales
+    (x's codes made with the static g_x, the GEMM2 input re-quantized with the
+    static g_a), the forward on handed-over codes equals the forward on x bit
+    for bit (stream path at T = 64, tiled at T = 1024)."""
+    L = synth.LAYERS[2]
+    print(f"layer 2 T={T} pre-quantized: shared expert, static scales", flush=True)
+    x, logits = synth.activations(2, T), synth.router_logits(2, T)
+    lg = torch.from_numpy(logits).cuda()
+    xd = to_device_bf16(x)
+    # shared expert: the weights hold E + 1 experts
+    wts = gpu_weights(2, n_experts=L.E + 1)
+    xc, xs, xg = oracle.quantize_rows(x)
+    layer = binding.MoeLayer(T, L.H, L.I, L.E, L.k, True, shared_expert="average")
+    layer.bind(wts)
+    ref = layer.forward(xd, lg)
+    got = layer.forward_quantized(_dev(xc), _dev(xs), _dev(xg), lg)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    layer.close()
+    del wts
+    # static scales: g_x for x's codes, g_a for the GEMM2 input
+    gx = float(oracle.global_scale(synth.bf16_to_f32(x)))
+    ga = 40.0
+    sc, ss = oracle.quantize_rows_given_g(synth.bf16_to_f32(x), gx)
+    sg = np.full(T, gx, np.float32)
+    layer = binding.MoeLayer(T, L.H, L.I, L.E, L.k, True, static_act_scales=True)
+    layer.bind(_weights(2))
+    layer.set_act_scales(torch.tensor([gx, ga], dtype=torch.float32, device="cuda"))
+    ref = layer.forward(xd, lg)
+    got = layer.forward_quantized(_dev(sc), _dev(ss), _dev(sg), lg)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    layer.close()
