@@ -71,10 +71,25 @@ const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
 // [OFP8] E4M3 decode: e = bits 6..3, m = bits 2..0, bias 7; e == 0 is
 // subnormal (m/8 * 2^-6).  Only the 127 finite non-negative codes are used.
-double e4m3_value(uint8_t b) {
+double e4m3_decode(uint8_t b) {
   int e = (b >> 3) & 15, m = b & 7;
   if (e == 0) return std::ldexp(m / 8.0, -6);
   return std::ldexp(1.0 + m / 8.0, e - 7);
+}
+
+// The decode above for all 256 bytes, computed once (the encoder searches
+// and the dequantization look values up instead of calling ldexp each time;
+// the values are the same).
+struct E4M3Table {
+  double v[256];
+  E4M3Table() {
+    for (int b = 0; b < 256; ++b) v[b] = e4m3_decode(static_cast<uint8_t>(b));
+  }
+};
+
+double e4m3_value(uint8_t b) {
+  static const E4M3Table table;
+  return table.v[b];
 }
 
 }  // namespace
@@ -105,10 +120,12 @@ ORC_API uint8_t orc_e2m1_encode(float v) {
   return static_cast<uint8_t>(sign | best);
 }
 
-ORC_API double orc_e2m1_value(uint8_t code) {
+static double e2m1_value(uint8_t code) {
   double v = kE2M1[code & 7];
   return (code & 8) ? -v : v;
 }
+
+ORC_API double orc_e2m1_value(uint8_t code) { return e2m1_value(code); }
 
 // [OFP8] E4M3 encode of a non-negative finite scale with saturation to 448
 // (0x7E): the nearest of the 127 finite codes 0x00..0x7E, ties to even code.
@@ -255,7 +272,7 @@ ORC_API void orc_dequantize(const uint8_t* codes, const uint8_t* S, const float*
       uint8_t byte = codes[r * (K / 2) + k / 2];
       uint8_t c = (k & 1) ? (byte >> 4) : (byte & 15);
       double d = e4m3_value(S[r * (K / 16) + k / 16]);
-      out[r * K + k] = orc_e2m1_value(c) * d / gr;
+      out[r * K + k] = e2m1_value(c) * d / gr;
     }
   }
 }
@@ -352,10 +369,13 @@ struct LayerArgs {
 void dequant_rows(const uint8_t* codes, const uint8_t* S, double g, int64_t rows, int64_t K,
                   double* out) {
   for (int64_t r = 0; r < rows; ++r)
-    for (int64_t k = 0; k < K; ++k) {
-      uint8_t byte = codes[r * (K / 2) + k / 2];
-      uint8_t c = (k & 1) ? (byte >> 4) : (byte & 15);
-      out[r * K + k] = orc_e2m1_value(c) * e4m3_value(S[r * (K / 16) + k / 16]) / g;
+    for (int64_t b = 0; b < K / 16; ++b) {
+      const double d = e4m3_value(S[r * (K / 16) + b]);  // the block's scale
+      for (int64_t k = 16 * b; k < 16 * b + 16; ++k) {
+        uint8_t byte = codes[r * (K / 2) + k / 2];
+        uint8_t c = (k & 1) ? (byte >> 4) : (byte & 15);
+        out[r * K + k] = e2m1_value(c) * d / g;
+      }
     }
 }
 
