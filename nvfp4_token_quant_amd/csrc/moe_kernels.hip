@@ -30,11 +30,13 @@ namespace nvfp4 {
 // ---------------------------------------------------------------------------
 // Router reductions.  A candidate is the 64-bit key (order-preserving bits of
 // the logit) << 32 | ~expert, so the larger key is the larger logit and, on
-// equal logits, the smaller expert index.  Reductions over a 16-lane DPP row
-// use quad permutes (xor 1, xor 2) and row rotates (4, 8), a few cycles each.
+// equal logits, the smaller expert index.  -0.0 is keyed as +0.0: a binary32
+// comparison finds the two equal, so their tie also goes to the smaller
+// index.  Reductions over a 16-lane DPP row use quad permutes (xor 1, xor 2)
+// and row rotates (4, 8), a few cycles each.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
-  const uint32_t u = __float_as_uint(v);
+  const uint32_t u = __float_as_uint(v) == 0x80000000u ? 0u : __float_as_uint(v);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~e);
 }

@@ -42,6 +42,21 @@ def test_router_ties_go_to_smaller_index():
     np.testing.assert_allclose(w[0, :3], w[0, 0])
 
 
+def test_router_signed_zero_ties():
+    """-0.0 and +0.0 compare equal in binary32, so they tie like any equal
+    logits: the smaller expert index wins and the slot order follows the
+    index.  Checked against a sort on (-value, index) in Python floats,
+    where -0.0 == 0.0 as well."""
+    rng = np.random.default_rng(12)
+    vals = np.array([-0.0, 0.0, 1.0, -1.0, 0.5], np.float32)
+    logits = rng.choice(vals, size=(200, 12)).astype(np.float32)
+    ids, w = oracle.router(logits, 5)
+    for t in range(logits.shape[0]):
+        want = sorted(range(12), key=lambda e: (-float(logits[t, e]), e))[:5]
+        assert ids[t].tolist() == want
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
 def test_permutation_matches_stable_argsort():
     rng = np.random.default_rng(11)
     T, k, E = 500, 8, 40
