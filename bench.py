@@ -3,10 +3,15 @@
 One step = one forward of the whole layer (per-token quantize, router top-k,
 expandInputRows permutation, GEMM1 + SwiGLU, re-quantization + GEMM2,
 finalize) over one batch of seeded synthetic tokens already resident in HBM.
-Default workload: the decode-shaped layer (T=64, H=2048, E=128, top-8,
-I=768).  `--layer 4` times the quantize-only workload instead (per-token
-NVFP4 quantization of x bf16 [16384, 7168]; one step = one launch).  Prints
-one JSON line.
+Default run: the decode-shaped layer (T=64, H=2048, E=128, top-8, I=768) is
+the headline line, and a `configs` list in the same JSON line times every
+other configuration the same way in the same run: the tiny layer (T=16), the
+prefill-shaped layer (T=4096, Zipf-skewed routing; MFMA roofline), the
+quantize-only workload (per-token NVFP4 quantization of x bf16 [16384, 7168];
+one step = one launch, HBM roofline) and the large layer (H=7168, E=256,
+I=2048) at T = 1, 7 and 2048, each with its own roofline and CPU-oracle
+baseline.  `--layer N [--T T]` times one workload alone.  Prints one JSON
+line.
 
 Timing: `steps` forwards after `warmup` untimed ones, bracketed by
 synchronizations; wall time gives `value` (tokens/s).  By default the timed
@@ -69,7 +74,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layer", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layer", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="time this workload alone (default: the decode layer plus every config)")
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the layer's)")
     ap.add_argument("--fast-finalize", action="store_true",
                     help="atomic (non-deterministic) finalize instead of the slot-ordered one")
@@ -84,6 +90,10 @@ def parse():
                          "scales, global scales made once before timing), the runner contract")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--config-cpu-budget-s", type=float, default=4.0,
+                    help="CPU-oracle budget of each entry of the configs list")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default run: only the decode headline, without the configs list")
     ap.add_argument("--eager", action="store_true",
                     help="launch the kernels directly instead of replaying captured HIP graphs")
     ap.add_argument("--copy-reference", action="store_true",
@@ -115,6 +125,9 @@ class Hip:
         self.h.hipEventDestroy(e)
 
 
+CONFIGS = [(1, 16), (3, 4096), (4, None), (5, 1), (5, 7), (5, 2048)]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -124,34 +137,73 @@ def main():
     if args.prequantized and args.w4a16:
         print("--prequantized applies to NVFP4 activations; --w4a16 takes bf16 ones", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     from nvfp4_token_quant_amd import binding, synth
-    from nvfp4_token_quant_amd.workloads import gpu_weights, to_device_bf16
 
     if args.copy_reference:
         return copy_reference(args)
     binding.lib()  # fails loudly if the HIP library is missing
-    if args.layer == 4:
-        return bench_quantize(args)
-    L = synth.LAYERS[args.layer]
-    T = args.T or L.T
+    torch.cuda.set_device(torch.device("cuda:0"))
+    if args.layer is not None:
+        res = bench_quantize(args, args.T, args.cpu_budget_s) if args.layer == 4 else \
+            bench_layer(args, args.layer, args.T or synth.LAYERS[args.layer].T, args.cpu_budget_s)
+        print(json.dumps(res), flush=True)
+        return
+    res = bench_layer(args, 2, synth.LAYERS[2].T, args.cpu_budget_s)
+    if not args.no_configs:
+        configs = []
+        for lid, T in CONFIGS:
+            e = bench_quantize(args, T, args.config_cpu_budget_s) if lid == 4 else \
+                bench_layer(args, lid, T, args.config_cpu_budget_s)
+            configs.append({key: e[key] for key in ("config", "value", "unit", "ms_per_step", "roofline",
+                                                   "layer_roofline", "cpu_baseline") if key in e})
+            print(f"bench: {e['config']['workload']} T={e['config']['T']}: {e['ms_per_step']:.4f} ms/step, "
+                  f"{e['roofline']['bound']} frac {e['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+        res["configs"] = configs
+    print(json.dumps(res), flush=True)
+
+
+_WEIGHT_CACHE = {}
+
+
+def layer_weights(layer_id, n_experts, rotate, dev):
+    """Packed weights of a layer, `rotate` copies, kept for the next entry of
+    the same layer (the large layer is timed at three batch sizes)."""
+    import torch
+
+    from nvfp4_token_quant_amd.workloads import gpu_weights
+    key = (layer_id, n_experts, rotate)
+    if key not in _WEIGHT_CACHE:
+        _WEIGHT_CACHE.clear()
+        torch.cuda.empty_cache()
+        w = [gpu_weights(layer_id, device=dev, n_experts=n_experts)]
+        for _ in range(rotate - 1):
+            w.append(w[0].clone())
+        _WEIGHT_CACHE[key] = w
+    return _WEIGHT_CACHE[key]
+
+
+def bench_layer(args, layer_id, T, cpu_budget_s):
+    """One MoE-layer workload: the timed forwards, their stage rooflines and
+    the oracle baseline; returns the result record."""
+    import numpy as np
+    import torch
+
+    from nvfp4_token_quant_amd import binding, synth
+    from nvfp4_token_quant_amd.workloads import to_device_bf16
+
+    L = synth.LAYERS[layer_id]
     H, I, E, k = L.H, L.I, L.E, L.k
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print(f"bench: layer {args.layer} ({L.name}) T={T} H={H} E={E} k={k} I={I}", file=sys.stderr, flush=True)
+    print(f"bench: layer {layer_id} ({L.name}) T={T} H={H} E={E} k={k} I={I}", file=sys.stderr, flush=True)
 
-    x_bits = synth.activations(args.layer, T)
-    logits_np = synth.router_logits(args.layer, T)
+    x_bits = synth.activations(layer_id, T)
+    logits_np = synth.router_logits(layer_id, T)
     x = to_device_bf16(x_bits, dev)
     logits = torch.from_numpy(logits_np).to(dev)
     n_shared = 1 if args.shared else 0
-    weights = [gpu_weights(args.layer, device=dev, n_experts=E + n_shared)]
-    for _ in range(args.rotate - 1):
-        w0 = weights[0]
-        weights.append(binding.NvFp4Weights(*(t.clone() for t in (
-            w0.w13_codes, w0.w13_scales, w0.w13_gscale, w0.w2_codes, w0.w2_scales, w0.w2_gscale))))
+    weights = layer_weights(layer_id, E + n_shared, args.rotate, dev)
     det = not args.fast_finalize
     max_tokens = max(T, L.max_tokens)
     layers = []
@@ -283,7 +335,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, x_bits, T, H, I, k, L.E)
+        cpu = cpu_baseline(args, layer_id, x_bits, T, H, I, k, L.E, cpu_budget_s)
 
     for ly in layers:
         ly.close()
@@ -301,7 +353,7 @@ def main():
         "dtype": ("bf16 activations, nvfp4 weights, bf16 MFMA, f32 accumulate" if args.w4a16 else
                   "nvfp4 (e2m1 + e4m3 block-16 + f32 global) operands, f16 MFMA, f32 accumulate"),
         "data": "synthetic (seeded; weights from Philox4x64-10, quantized on the device)",
-        "config": {"workload": workload, "layer_id": args.layer, "T": T, "H": H,
+        "config": {"workload": workload, "layer_id": layer_id, "T": T, "H": H,
                    "E": E, "top_k": k, "I": I, "finalize": "deterministic" if det else "atomic",
                    "shared_expert": args.shared,
                    "activations": "bf16 (W4A16)" if args.w4a16 else
@@ -313,7 +365,7 @@ def main():
         "layer_roofline": layer_roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def copy_reference(args):
@@ -329,9 +381,10 @@ def copy_reference(args):
     print(json.dumps({"copy_reference_bytes": n, "copies": args.steps}), flush=True)
 
 
-def bench_quantize(args):
+def bench_quantize(args, T, cpu_budget_s):
     """Quantize-only workload: one step = one nvfp4_quantize_per_token launch
-    over x bf16 [T, H] (read 2 B, write 0.5625 B per element + 4 B per row)."""
+    over x bf16 [T, H] (read 2 B, write 0.5625 B per element + 4 B per row);
+    returns the result record."""
     import numpy as np
     import torch
 
@@ -339,10 +392,9 @@ def bench_quantize(args):
     from nvfp4_token_quant_amd.workloads import to_device_bf16
 
     L = synth.LAYERS[4]
-    T = args.T or L.T
+    T = T or L.T
     H = L.H
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     print(f"bench: layer 4 ({L.name}) T={T} H={H}", file=sys.stderr, flush=True)
     x_bits = synth.activations(4, T)
     nrot = max(1, args.rotate)
@@ -368,7 +420,7 @@ def bench_quantize(args):
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_quantize(args, x_bits)
+        cpu = cpu_baseline_quantize(x_bits, cpu_budget_s)
     result = {
         "metric": "NVFP4 MoE layer tokens/s + % roofline (HBM GB/s decode, MFMA prefill)",
         "value": T * args.steps / (t1 - t0),
@@ -391,10 +443,10 @@ def bench_quantize(args):
                      "kernel_ms": kernel_ms, "bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(result), flush=True)
+    return result
 
 
-def cpu_baseline_quantize(args, x_bits):
+def cpu_baseline_quantize(x_bits, budget_s):
     """The oracle's per-row quantizer, as it stands, on a bounded sample of rows."""
     import oracle
 
@@ -404,9 +456,9 @@ def cpu_baseline_quantize(args, x_bits):
     t0 = time.perf_counter()
     oracle.quantize_rows(x_bits[:n])
     per_row = (time.perf_counter() - t0) / n
-    n = int(min(T, max(n, args.cpu_budget_s / max(per_row, 1e-9))))
+    n = int(min(T, max(n, budget_s / max(per_row, 1e-9))))
     reps, dt = 0, 0.0
-    while dt < args.cpu_budget_s * 0.8 or reps == 0:
+    while dt < budget_s * 0.8 or reps == 0:
         t0 = time.perf_counter()
         oracle.quantize_rows(x_bits[:n])
         dt += time.perf_counter() - t0
@@ -415,18 +467,22 @@ def cpu_baseline_quantize(args, x_bits):
             "sample": f"first {n} of {T} rows x {reps} repetitions ({dt:.1f} s)"}
 
 
-def cpu_baseline(args, x_bits, T, H, I, k, E):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(args, layer_id, x_bits, T, H, I, k, E, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    tokens of the batch (all of it if the budget allows), the whole forward
+    in binary64 with the expert weights prepared before timing, repeated to
+    about budget_s.  On the large layer the sample is at most 8 tokens (each
+    of its experts costs the oracle about a second to prepare)."""
     import numpy as np
 
     import oracle
     from nvfp4_token_quant_amd import synth
     from tests.layer_fixtures import oracle_expert, oracle_weights
 
-    ids, w = oracle.router(synth.router_logits(args.layer, T), k)
+    ids, w = oracle.router(synth.router_logits(layer_id, T), k)
     shared = None
     if args.shared:
-        shared = oracle.QuantWeights(np.array([E], np.int32), *(a[None] for a in oracle_expert(args.layer, E)))
+        shared = oracle.QuantWeights(np.array([E], np.int32), *(a[None] for a in oracle_expert(layer_id, E)))
 
     xq = oracle.quantize_rows(x_bits) if args.prequantized else None
 
@@ -437,19 +493,19 @@ def cpu_baseline(args, x_bits, T, H, I, k, E):
             return oracle.moe_layer(x_bits, ids, w, toks, H, I, qw, a16=args.w4a16)
         return oracle.moe_layer_shared(x_bits, ids, w, toks, H, I, qw, shared, args.shared, a16=args.w4a16)
     rng = np.random.default_rng(0)
-    n = T
+    cap = 8 if H * I >= 7168 * 2048 else T
     toks = np.arange(T)
-    # grow the sample until it costs about cpu_budget_s (the oracle is linear in tokens)
+    # grow the sample until it costs about budget_s (the oracle is linear in tokens)
     probe = toks[: max(1, min(T, 4))]
-    qw = oracle_weights(args.layer, np.unique(ids[probe]))
+    qw = oracle_weights(layer_id, np.unique(ids[probe]))
     t0 = time.perf_counter()
     run(probe, qw)
     t_probe = time.perf_counter() - t0
-    n = int(min(T, max(len(probe), args.cpu_budget_s / max(t_probe / len(probe), 1e-6))))
+    n = int(min(T, cap, max(len(probe), budget_s / max(t_probe / len(probe), 1e-6))))
     toks = np.sort(rng.choice(T, n, replace=False)) if n < T else toks
-    qw = oracle_weights(args.layer, np.unique(ids[toks]))
+    qw = oracle_weights(layer_id, np.unique(ids[toks]))
     reps, dt = 0, 0.0
-    while dt < args.cpu_budget_s * 0.8 or reps == 0:   # repeat small samples to ~the budget
+    while dt < budget_s * 0.8 or reps == 0:   # repeat small samples to ~the budget
         t0 = time.perf_counter()
         run(toks, qw)
         dt += time.perf_counter() - t0

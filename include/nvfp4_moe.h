@@ -44,7 +44,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_TOO_MANY_TOKENS = 2,  /* T above the workspace's max_num_tokens */
   NVFP4_ERR_ALIAS = 3,            /* output overlaps an input */
   NVFP4_ERR_NO_WEIGHTS = 4,       /* forward before moe_workspace_bind_weights */
-  NVFP4_ERR_METADATA_CHANGED = 5, /* refresh with other dims / addresses */
+  NVFP4_ERR_METADATA_CHANGED = 5, /* refresh with other dims */
   NVFP4_ERR_HIP = 6,              /* HIP runtime or launch error */
   NVFP4_ERR_OOM = 7               /* device allocation failed */
 } nvfp4_status;
@@ -148,14 +148,16 @@ typedef struct moe_config {
   uint32_t flags;         /* OR of the MOE_* flags above, or 0 */
 } moe_config;
 
-/* NVFP4 expert weights, device pointers.  w13 rows [0, I) are the gate
- * projection (w1) and rows [I, 2I) the up projection (w3); act = silu(gate)*up.
+/* NVFP4 expert weights in the row-major boundary layout, device pointers
+ * (the input of moe_pack_weights; refresh_scales_inplace takes the scales in
+ * this layout).  w13 rows [0, I) are the gate projection (w1) and rows
+ * [I, 2I) the up projection (w3); act = silu(gate) * up.
  *   w13_codes  u8 [E, 2I, H/2], 16-byte aligned   w13_scales u8 [E, 2I, H/16]
  *   w13_gscale f32 [E]                            (per-expert global scale)
  *   w2_codes   u8 [E, H, I/2],  16-byte aligned   w2_scales  u8 [E, H, I/16]
  *   w2_gscale  f32 [E]
- * The dims must equal the workspace's: num_experts = E, or E + 1 with
- * MOE_SHARED_EXPERT (expert E is the shared one), and (H, I). */
+ * For a workspace the dims must equal its own: num_experts = E, or E + 1
+ * with MOE_SHARED_EXPERT (expert E is the shared one), and (H, I). */
 typedef struct moe_nvfp4_weights {
   int64_t num_experts, hidden, inter;
   const void* w13_codes;
@@ -165,6 +167,50 @@ typedef struct moe_nvfp4_weights {
   const void* w2_scales;
   const float* w2_gscale;
 } moe_nvfp4_weights;
+
+/* Expert weights packed for the kernels, in caller-owned device memory.
+ * w13 and w2 each hold the matrix's codes and block scales as "unit
+ * records": a unit is four 16-row MMA fragments of one expert (for W13 gate
+ * rows 32j..32j+31 with the matching up rows I+32j..; for W2 rows
+ * 64j..64j+63), and the record of (unit, 128-wide K step) is 4608 bytes (4 KB
+ * of codes, one lane's 32 codes per 16 bytes, then 512 bytes of their E4M3
+ * scales), so that one wave reads a record as five contiguous spans.  This is
+ * the kernels' analogue of the *_blockscale_mma copies of [P1]
+ * "Implementation breakdown" item 3, here for codes and scales together.
+ * Records are expert-major: expert e's records start at e times the
+ * per-expert size (moe_packed_bytes with num_experts = 1), so experts can be
+ * packed in pieces.
+ *   w13        u8 [moe_packed_bytes w13], 16-byte aligned
+ *   w13_gscale f32 [E]  per-expert global scales (copied at bind)
+ *   w2         u8 [moe_packed_bytes w2], 16-byte aligned
+ *   w2_gscale  f32 [E] */
+typedef struct moe_nvfp4_packed {
+  int64_t num_experts, hidden, inter;
+  const void* w13;
+  const float* w13_gscale;
+  const void* w2;
+  const float* w2_gscale;
+} moe_nvfp4_packed;
+
+/*
+ * Bytes of the packed W13 and W2 buffers for E experts of hidden size H and
+ * intermediate size I (multiples of 128).  Host-only, no device access.
+ * NVFP4_ERR_INVALID_ARG for bad dims or NULL outputs.
+ */
+int moe_packed_bytes(int64_t num_experts, int64_t hidden, int64_t inter, int64_t* w13_bytes,
+                     int64_t* w2_bytes);
+
+/*
+ * Pack row-major NVFP4 weights into the unit-record layout (the online
+ * weight conversion's last step, [P1] "Feature and motivation"; done once
+ * per weight load).  w13_packed_dev / w2_packed_dev are caller-owned device
+ * buffers of moe_packed_bytes(w->num_experts, ...) bytes, 16-byte aligned,
+ * not overlapping the inputs.  With NULL code pointers in `w` only the
+ * scale bytes of the records are written (the codes already there stay).
+ * The global scales in `w` are not read.  Enqueued on `stream`; the inputs
+ * must stay valid until that work has run.
+ */
+int moe_pack_weights(const moe_nvfp4_weights* w, void* w13_packed_dev, void* w2_packed_dev, void* stream);
 
 typedef struct moe_workspace moe_workspace;
 
@@ -183,16 +229,16 @@ typedef struct moe_workspace moe_workspace;
 int moe_workspace_create(const moe_config* cfg, void* stream, moe_workspace** out);
 
 /*
- * Bind expert weights.  Codes, block scales and global scales are COPIED
- * into library-owned buffers in the kernels' unit-record layout (the
- * *_blockscale_mma analogue of [P1] "Implementation breakdown" item 3; one
- * wave load then reads 1 KB of contiguous memory).  The caller's code
- * addresses are remembered: a later refresh_scales_inplace re-reads the
- * codes from the same addresses (weights reloaded in place).  May be called
- * once per workspace.  Enqueued on `stream`; the caller's buffers must stay
- * valid until that work has run.
+ * Bind packed expert weights (moe_pack_weights).  The packed records are
+ * BORROWED: the caller owns them and must keep them alive, at the same
+ * addresses, for as long as the workspace runs forwards; reloading codes in
+ * place (moe_pack_weights into the same buffers) is picked up by the next
+ * forward, captured graphs included.  The per-expert global scales are
+ * COPIED into library-owned buffers.  May be called once per workspace.
+ * Enqueued on `stream`; the global-scale arrays must stay valid until that
+ * copy has run.  Dims must match the workspace (NVFP4_ERR_INVALID_ARG).
  */
-int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
+int moe_workspace_bind_weights(moe_workspace* ws, const moe_nvfp4_packed* w, void* stream);
 
 /*
  * Forward of the layer on T tokens:
@@ -246,15 +292,17 @@ int moe_nvfp4_forward_quantized(moe_workspace* ws, const void* x_codes_dev, cons
                                 void* out_dev, void* stream);
 
 /*
- * Reload after the caller updated the weights in place ([P1]
- * "Implementation breakdown" item 3 and "Source snippets",
- * refresh_cutedsl_standard_scales_for_weight_update): the codes (re-read
- * from the bound addresses), the new block scales and the global scales are
- * copied INTO the existing library buffers, so addresses captured by a HIP
- * graph stay valid.  `w` must carry the bound dims and the bound code
- * pointers (or NULL code pointers); any difference returns
- * NVFP4_ERR_METADATA_CHANGED ("recapture is required") and changes nothing.
- * Enqueued on `stream`, ordered with forwards on the same stream.
+ * Scale reload after a weight update ([P1] "Implementation breakdown" item 3
+ * and "Source snippets", refresh_cutedsl_standard_scales_for_weight_update):
+ * the new block scales are written INTO the bound packed records (the
+ * caller's buffers, at the addresses bound) and the new global scales INTO
+ * the workspace's copies, so addresses captured by a HIP graph stay valid.
+ * `w` carries the new scales in the row-major layout; its code pointers must
+ * be NULL (the codes live in the caller's packed buffers and are reloaded
+ * there with moe_pack_weights; otherwise NVFP4_ERR_INVALID_ARG).  Dims that
+ * differ from the bound ones return NVFP4_ERR_METADATA_CHANGED
+ * ("recapture is required") and change nothing.  Enqueued on `stream`,
+ * ordered with forwards on the same stream.
  */
 int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* stream);
 
@@ -271,8 +319,8 @@ int refresh_scales_inplace(moe_workspace* ws, const moe_nvfp4_weights* w, void* 
  */
 int moe_workspace_set_act_scales(moe_workspace* ws, const float* scales_dev, void* stream);
 
-/* Free library-owned memory (never the caller's codes).  NULL is a no-op.
- * Synchronizes the device. */
+/* Free library-owned memory (never the caller's packed weights).  NULL is a
+ * no-op.  Synchronizes the device. */
 int moe_workspace_destroy(moe_workspace* ws);
 
 /*

@@ -53,6 +53,12 @@ class MoeWeights(ctypes.Structure):
                 ("w2_scales", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p)]
 
 
+class MoePacked(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int64), ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64),
+                ("w13", ctypes.c_void_p), ("w13_gscale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p)]
+
+
 _lib = None
 _synth = None
 _P = ctypes.c_void_p
@@ -74,8 +80,12 @@ def lib():
         L.nvfp4_quantize_experts.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]
         L.moe_workspace_create.restype = ctypes.c_int
         L.moe_workspace_create.argtypes = [ctypes.POINTER(MoeConfig), _P, ctypes.POINTER(_P)]
+        L.moe_packed_bytes.restype = ctypes.c_int
+        L.moe_packed_bytes.argtypes = [_I64, _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+        L.moe_pack_weights.restype = ctypes.c_int
+        L.moe_pack_weights.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P]
         L.moe_workspace_bind_weights.restype = ctypes.c_int
-        L.moe_workspace_bind_weights.argtypes = [_P, ctypes.POINTER(MoeWeights), _P]
+        L.moe_workspace_bind_weights.argtypes = [_P, ctypes.POINTER(MoePacked), _P]
         L.moe_nvfp4_forward.restype = ctypes.c_int
         L.moe_nvfp4_forward.argtypes = [_P, _P, _P, _I64, _P, _P]
         L.moe_nvfp4_forward_quantized.restype = ctypes.c_int
@@ -212,7 +222,9 @@ def synth_weights(seed: int, tag: int, expert0: int, experts: int, shape, sigma:
 # --- MoE layer -------------------------------------------------------------------
 
 class NvFp4Weights:
-    """NVFP4 expert weights held in torch device tensors."""
+    """NVFP4 expert weights in the row-major boundary layout (torch device
+    tensors).  Codes may be None (a scales-only descriptor, for
+    refresh_scales and scale-only packing)."""
 
     def __init__(self, w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale):
         self.w13_codes, self.w13_scales, self.w13_gscale = w13_codes, w13_scales, w13_gscale
@@ -220,16 +232,80 @@ class NvFp4Weights:
 
     @property
     def dims(self):
-        E, two_i, half_h = self.w13_codes.shape
-        return E, half_h * 2, two_i // 2
+        E, two_i, h16 = self.w13_scales.shape
+        return E, h16 * 16, two_i // 2
 
     def desc(self, with_codes=True) -> MoeWeights:
         E, H, I = self.dims
+        has = with_codes and self.w13_codes is not None
         return MoeWeights(E, H, I,
-                          self.w13_codes.data_ptr() if with_codes else None,
+                          self.w13_codes.data_ptr() if has else None,
                           self.w13_scales.data_ptr(), self.w13_gscale.data_ptr(),
-                          self.w2_codes.data_ptr() if with_codes else None,
+                          self.w2_codes.data_ptr() if has else None,
                           self.w2_scales.data_ptr(), self.w2_gscale.data_ptr())
+
+
+def packed_bytes(num_experts, hidden, inter):
+    """(W13 bytes, W2 bytes) of the packed unit records of num_experts experts."""
+    b13, b2 = _I64(), _I64()
+    _check(lib().moe_packed_bytes(num_experts, hidden, inter, ctypes.byref(b13), ctypes.byref(b2)))
+    return b13.value, b2.value
+
+
+class PackedWeights:
+    """Expert weights packed into the kernels' unit records, in caller-owned
+    device tensors: w13 / w2 uint8 [E, bytes per expert], global scales
+    float32 [E].  A layer bound to them borrows the records (keep them
+    alive); experts are contiguous, so [a:b] slices select experts."""
+
+    def __init__(self, hidden, inter, w13, w13_gscale, w2, w2_gscale):
+        self.hidden, self.inter = hidden, inter
+        self.w13, self.w13_gscale, self.w2, self.w2_gscale = w13, w13_gscale, w2, w2_gscale
+
+    @classmethod
+    def empty(cls, num_experts, hidden, inter, device="cuda"):
+        b13, b2 = packed_bytes(1, hidden, inter)
+        return cls(hidden, inter,
+                   torch.empty((num_experts, b13), dtype=torch.uint8, device=device),
+                   torch.empty((num_experts,), dtype=torch.float32, device=device),
+                   torch.empty((num_experts, b2), dtype=torch.uint8, device=device),
+                   torch.empty((num_experts,), dtype=torch.float32, device=device))
+
+    @property
+    def num_experts(self):
+        return self.w13.shape[0]
+
+    def experts(self, a, b):
+        """The packed weights of experts a .. b - 1 (views, no copy)."""
+        return PackedWeights(self.hidden, self.inter, self.w13[a:b], self.w13_gscale[a:b],
+                             self.w2[a:b], self.w2_gscale[a:b])
+
+    def clone(self):
+        return PackedWeights(self.hidden, self.inter, self.w13.clone(), self.w13_gscale.clone(),
+                             self.w2.clone(), self.w2_gscale.clone())
+
+    def desc(self) -> MoePacked:
+        for t in (self.w13, self.w2, self.w13_gscale, self.w2_gscale):
+            if not t.is_contiguous():
+                raise ValueError("packed weight tensors must be contiguous")
+        return MoePacked(self.num_experts, self.hidden, self.inter, self.w13.data_ptr(),
+                         self.w13_gscale.data_ptr(), self.w2.data_ptr(), self.w2_gscale.data_ptr())
+
+
+def pack_weights(w: NvFp4Weights, out: PackedWeights = None, stream=None) -> PackedWeights:
+    """Pack row-major NVFP4 weights (moe_pack_weights) into `out` (new
+    tensors if None); without codes in `w` only the scale bytes are written.
+    The global scales are copied into out as well."""
+    E, H, I = w.dims
+    if out is None:
+        out = PackedWeights.empty(E, H, I, device=w.w13_scales.device)
+    if out.num_experts != E or out.hidden != H or out.inter != I:
+        raise ValueError("packed buffers of other dims")
+    d = w.desc(with_codes=w.w13_codes is not None)
+    _check(lib().moe_pack_weights(ctypes.byref(d), _ptr(out.w13), _ptr(out.w2), _stream(stream)))
+    out.w13_gscale.copy_(w.w13_gscale)
+    out.w2_gscale.copy_(w.w2_gscale)
+    return out
 
 
 class MoeLayer:
@@ -253,13 +329,19 @@ class MoeLayer:
         self.handle = h
         self.weights = None
 
-    def bind(self, weights: NvFp4Weights, stream=None):
+    def bind(self, weights, stream=None):
+        """Bind PackedWeights (borrowed: the layer keeps a reference), or
+        NvFp4Weights, which are packed into new tensors first."""
+        if isinstance(weights, NvFp4Weights):
+            weights = pack_weights(weights, stream=stream)
         d = weights.desc()
         _check(lib().moe_workspace_bind_weights(self.handle, ctypes.byref(d), _stream(stream)))
         self.weights = weights
 
-    def refresh_scales(self, weights: NvFp4Weights, with_codes=True, stream=None):
-        d = weights.desc(with_codes)
+    def refresh_scales(self, weights: NvFp4Weights, stream=None):
+        """New block and global scales (codes not read) written in place
+        into the bound packed records and the layer's global scales."""
+        d = weights.desc(with_codes=False)
         _check(lib().refresh_scales_inplace(self.handle, ctypes.byref(d), _stream(stream)))
 
     def set_act_scales(self, scales, stream=None):

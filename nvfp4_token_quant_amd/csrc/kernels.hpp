@@ -151,7 +151,8 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* events);
 // Copy row-major codes [E, N, K/2] and scales [E, N, K/16] of one weight
 // matrix into unit records.  w13: N = 2I, split = 1 (gate / up halves);
-// w2: N = H, split = 0.  N % 64 == 0, K % 128 == 0.
+// w2: N = H, split = 0.  N % 64 == 0, K % 128 == 0.  codes == nullptr:
+// only the records' scale bytes are written.
 hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, uint8_t* dst,
                                int64_t E, int64_t N, int64_t K, int split, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);

@@ -721,25 +721,29 @@ __device__ __forceinline__ int64_t unit_fragment_row(int64_t u, int f, int64_t N
   return e * N + r;
 }
 
+// codes == nullptr: only the scale chunks are written (the records' codes
+// stay as they are), one thread per scale chunk.
 __global__ void pack_weights_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                     uint8_t* __restrict__ dst, int64_t units, int64_t N, int K,
                                     int split) {
   constexpr int kChunks = kRecBytes / 16;
+  constexpr int kCodeChunks = kRecCodeBytes / 16;
   const int S = ksteps(K);
+  const int per_rec = codes ? kChunks : kChunks - kCodeChunks;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= units * S * kChunks) return;
-  const int64_t rec = c / kChunks;
-  const int w = static_cast<int>(c - rec * kChunks);
+  if (c >= units * S * per_rec) return;
+  const int64_t rec = c / per_rec;
+  const int w = static_cast<int>(c - rec * per_rec) + (codes ? 0 : kCodeChunks);
   const int64_t u = rec / S;
   const int s = static_cast<int>(rec - u * S);
   uint4 v;
-  if (w < kRecCodeBytes / 16) {
+  if (w < kCodeChunks) {
     const int f = w / 64, l = w % 64;
     const int64_t row = unit_fragment_row(u, f, N, split) + (l & 15);
     v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * s + 16 * (l >> 4));
   } else {
     uint8_t out[16];
-    const int l0 = 2 * (w - kRecCodeBytes / 16);
+    const int l0 = 2 * (w - kCodeChunks);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int l = l0 + h;
@@ -753,7 +757,7 @@ __global__ void pack_weights_kernel(const uint8_t* __restrict__ codes, const uin
     }
     __builtin_memcpy(&v, out, 16);
   }
-  *reinterpret_cast<uint4*>(dst + c * 16) = v;
+  *reinterpret_cast<uint4*>(dst + (rec * kChunks + w) * 16) = v;
 }
 
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
@@ -764,7 +768,8 @@ __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict
 hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, uint8_t* dst,
                                int64_t E, int64_t N, int64_t K, int split, hipStream_t s) {
   const int64_t units = E * (N / 64);
-  const int64_t n = units * ksteps(static_cast<int>(K)) * (kRecBytes / 16);
+  const int per_rec = (codes ? kRecBytes : kRecBytes - kRecCodeBytes) / 16;
+  const int64_t n = units * ksteps(static_cast<int>(K)) * per_rec;
   pack_weights_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
       codes, scales, dst, units, N, static_cast<int>(K), split);
   return hipGetLastError();

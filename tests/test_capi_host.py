@@ -70,4 +70,21 @@ def test_workspace_config_checks():
     assert L.moe_nvfp4_forward(None, None, None, 1, None, None) == 1
     assert L.moe_nvfp4_forward_quantized(None, None, None, None, None, 1, None, None) == 1
     assert L.refresh_scales_inplace(None, None, None) == 1
+    assert L.moe_workspace_bind_weights(None, None, None) == 1
+    assert L.moe_pack_weights(None, None, None, None) == 1
     assert L.moe_workspace_destroy(None) == 0
+
+
+def test_packed_bytes_host_only():
+    """Packed unit-record sizes (host-only arithmetic, no device): four
+    16-row fragments x 128-wide K steps x 4608-byte records, i.e. the NVFP4
+    bytes of the matrix (0.5 + 1/16 B per element) exactly."""
+    from nvfp4_token_quant_amd import binding
+    for E, H, I in ((8, 256, 512), (128, 2048, 768), (256, 7168, 2048), (1, 128, 128)):
+        b13, b2 = binding.packed_bytes(E, H, I)
+        assert b13 == E * 2 * I * H * 9 // 16
+        assert b2 == E * H * I * 9 // 16
+        assert binding.packed_bytes(1, H, I) == (b13 // E, b2 // E)
+    for bad in ((0, 256, 512), (8, 200, 512), (8, 256, 100), (2000, 256, 512)):
+        with pytest.raises(binding.Nvfp4Error):
+            binding.packed_bytes(*bad)

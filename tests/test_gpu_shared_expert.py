@@ -109,8 +109,7 @@ def test_shared_ragged_batches_and_weight_count():
         np.testing.assert_array_equal(out, full[:T])
     layer.close()
     wts = _weights(2)
-    routed_only = binding.NvFp4Weights(wts.w13_codes[:L.E], wts.w13_scales[:L.E], wts.w13_gscale[:L.E],
-                                       wts.w2_codes[:L.E], wts.w2_scales[:L.E], wts.w2_gscale[:L.E])
+    routed_only = wts.experts(0, L.E)
     layer = binding.MoeLayer(L.T, L.H, L.I, L.E, L.k, True, shared_expert="sum")
     with pytest.raises(binding.Nvfp4Error) as ei:
         layer.bind(routed_only)
