@@ -76,30 +76,128 @@ def test_grid_midpoints_and_ties():
 
 
 @pytest.mark.timeout(600)
-def test_quantize_layer_full_size_sampled():
-    """The quantize-only workload [16384, 7168] at full size: sampled rows
-    bit-exact, plus properties on every row."""
+def test_quantize_layer_full_size():
+    """The quantize-only workload [16384, 7168] (Student-t(3) rows, every
+    97th row zero, 4 rows x1e3) at full size: codes, scale bytes and global
+    scales of every row bit-exact, plus the format's properties on every
+    row."""
     L = synth.LAYERS[4]
     x = synth.activations(4)
     print(f"quantize layer {L.T}x{L.H}", flush=True)
     c, s, g = _gpu_quant(x)
-    rng = np.random.default_rng(0)
+    oc, os_, og = oracle.quantize_rows(x)
+    np.testing.assert_array_equal(g.view(np.uint32), og.view(np.uint32))
+    np.testing.assert_array_equal(s, os_)
+    np.testing.assert_array_equal(c, oc)
     xf = synth.bf16_to_f32(x)
     amax = np.abs(xf).max(axis=1)
     zero = np.flatnonzero(amax == 0)
-    big = np.argsort(amax)[-4:]
-    sample = np.unique(np.concatenate([zero[:20], big, rng.choice(L.T, 300, replace=False),
-                                       [0, L.T - 1]]))
-    oc, os_, og = oracle.quantize_rows(x[sample])
-    np.testing.assert_array_equal(c[sample], oc)
-    np.testing.assert_array_equal(s[sample], os_)
-    np.testing.assert_array_equal(g[sample], og)
-    # every row: zero rows -> g 1, scales 0, codes 0; else the row-max block has 448
+    assert len(zero) == len(range(0, L.T, 97))
+    # zero rows -> g 1, scales 0, codes 0; else the row-max block has 448
     assert np.all(g[zero] == 1.0) and not s[zero].any() and not c[zero].any()
     nz = np.flatnonzero(amax > 0)
     top_block = np.argmax(np.abs(xf[nz]), axis=1) // 16
     assert np.all(s[nz, top_block] == 0x7E)
     np.testing.assert_array_equal(g[nz], (np.float32(2688.0) / amax[nz]).astype(np.float32))
+
+
+def _finite_bf16_patterns():
+    """Every finite bf16 bit pattern (both signs, zeros and subnormals
+    included; the 256 inf / NaN patterns left out)."""
+    b = np.arange(1 << 16, dtype=np.uint32)
+    return b[((b >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+
+
+def _pack_blocks(blocks, cols=16384):
+    """Rows of `cols` columns filled with 16-element blocks in the given
+    order (sorted by block magnitude so that one row's blocks lie within a
+    narrow range and keep nonzero E4M3 scales); each row's first block
+    carries the row's largest block maximum."""
+    nb = cols // 16
+    order = np.argsort(np.abs(synth.bf16_to_f32(blocks)).max(axis=1), kind="stable")
+    blocks = blocks[order]
+    rows = (len(blocks) + nb - 1) // nb
+    pad = rows * nb - len(blocks)
+    if pad:
+        blocks = np.concatenate([blocks, np.zeros((pad, 16), np.uint16)])
+    out = blocks.reshape(rows, nb, 16)
+    # move each row's largest block to the front (the order within a row does
+    # not change any block's result, only which block holds the row max)
+    mags = np.abs(synth.bf16_to_f32(out)).max(axis=2)
+    top = mags.argmax(axis=1)
+    r = np.arange(rows)
+    first = out[r, 0].copy()
+    out[r, 0] = out[r, top]
+    out[r, top] = first
+    return out.reshape(rows, cols)
+
+
+def _encoder_sweep_rows():
+    """Rows of the encoder sweep (see test_device_encoders_sweep)."""
+    pats = _finite_bf16_patterns()
+    vals = synth.bf16_to_f32(pats)
+    posv = vals[vals > 0]                        # ascending
+    cols = 16384
+    nb = cols // 16
+    rows = []
+    # block scales: row max M in block 0, then every positive a <= M as the
+    # maximum of one block [a, a/3, -a/7, 0, ...]
+    for M in (2.0 ** -126, 2.0 ** -60, 1e-3, 1.0, 6.0, 448.0, 2688.0, 3e5, 2.0 ** 64, 2.0 ** 127):
+        Mb = synth.bf16_to_f32(synth.bf16_bits(np.array([M], np.float32)))[0]
+        a = posv[posv <= Mb]
+        for i in range(0, len(a), nb - 1):
+            ch = a[i:i + nb - 1]
+            row = np.zeros((nb, 16), np.float32)
+            row[0, 0] = Mb
+            row[1:1 + len(ch), 0] = ch
+            row[1:1 + len(ch), 1] = ch / 3
+            row[1:1 + len(ch), 2] = -ch / 7
+            rows.append(synth.bf16_bits(row).reshape(cols))
+    x_scales = np.stack(rows)
+    # element codes: element v (and -v) in a block of maximum B = 6 |v| / t
+    # for t near each decision point; the blocks are sorted by B and packed
+    # into rows, so each row's blocks keep full-precision E4M3 scales
+    nz = pats[vals != 0]
+    nzv = np.abs(vals[vals != 0])
+    blocks = []
+    for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+        for f in (0.999, 1.0, 1.001):
+            with np.errstate(over="ignore"):
+                B = nzv * np.float32(6.0 / (t * f))
+            ok = np.isfinite(B) & (B < 3.0e38)
+            Bb = synth.bf16_bits(np.where(ok, B, 0).astype(np.float32))
+            ok &= synth.bf16_to_f32(Bb) >= nzv
+            blk = np.zeros((int(ok.sum()), 16), np.uint16)
+            blk[:, 0] = Bb[ok]
+            blk[:, 5] = nz[ok]
+            blk[:, 9] = nz[ok] ^ 0x8000
+            blocks.append(blk)
+    x = np.concatenate([x_scales, _pack_blocks(np.concatenate(blocks), cols)])
+    return x
+
+
+@pytest.mark.timeout(600)
+def test_device_encoders_sweep():
+    """The device's E4M3 and E2M1 encoders, driven through
+    nvfp4_quantize_per_token, against the oracle's encoders (written as
+    searches over the formats' values), bit for bit:
+      * block scales: every positive finite bf16 value as a block maximum,
+        under row maxima from 2^-126 to 2^127 (so every block scale
+        RN(RN(a * g) / 6) that a bf16 block can produce under those global
+        scales, saturation at 448 and underflow to 0 included);
+      * element codes: every finite bf16 value as a non-maximal element of a
+        block whose maximum puts it near each E2M1 decision point (0.25,
+        0.75, 1.25, 1.75, 2.5, 3.5, 5 after scaling) from both sides."""
+    x = _encoder_sweep_rows()
+    print(f"encoder sweep: {x.shape[0]} rows x {x.shape[1]}", flush=True)
+    c, s, g = _gpu_quant(x)
+    oc, os_, og = oracle.quantize_rows(x)
+    np.testing.assert_array_equal(g.view(np.uint32), og.view(np.uint32))
+    np.testing.assert_array_equal(s, os_)
+    np.testing.assert_array_equal(c, oc)
+    # the sweep reaches saturated, zero and subnormal scale bytes, every code
+    assert (s == 0x7E).any() and (s == 0).any() and ((s > 0) & (s < 8)).any()
+    assert len(np.unique(np.concatenate([c & 15, c >> 4]))) == 16
 
 
 def test_expert_quantizer_bit_exact():

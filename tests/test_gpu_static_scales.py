@@ -10,14 +10,17 @@ GPU's own act; tolerance: the layer output against the oracle's static layer.
 g_a is 3.7x the calibrated value, so the largest GEMM2 inputs saturate.
 Batch sizes cover the decode-sized, small-batch and three-kernel prologues and
 both re-quantization paths (fused into the GEMM2 stream kernel, and the
-separate kernel before the tiled GEMM2)."""
+separate kernel before the tiled GEMM2), up to the prefill-shaped layer at full
+size (T = 4096; its layer output on the tokens covering every expert's first
+and last expanded row)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from nvfp4_token_quant_amd import binding, synth
-from tests.layer_fixtures import bf16_tensor_to_f64, check_layer_tolerance, gpu_weights, oracle_weights, to_device_bf16
+from tests.layer_fixtures import (bf16_tensor_to_f64, check_layer_tolerance, covering_tokens, gpu_weights,
+                                  oracle_weights, to_device_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +47,8 @@ def _scales(layer_id, x, ids, w, T):
     return gx, ga
 
 
-@pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 256), (2, 64), (2, 301)])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 256), (2, 64), (2, 301), (3, 4096)])
 def test_static_scales_parity(layer_id, T):
     L = synth.LAYERS[layer_id]
     print(f"layer {layer_id} T={T} static scales", flush=True)
@@ -80,7 +84,13 @@ def test_static_scales_parity(layer_id, T):
     np.testing.assert_array_equal(a2c, c2)
     assert (a2s == 0x7E).any(), "the 3.7x g_a should saturate some block scales"
     # the layer against the oracle's static layer
-    toks = np.arange(T) if T <= 64 else np.array([0, 1, T // 2, T - 1])
+    if T <= 64:
+        toks = np.arange(T)
+    elif layer_id == 3:
+        toks, present, covered = covering_tokens(ids, L.E)
+        assert present <= covered
+    else:
+        toks = np.array([0, 1, T // 2, T - 1])
     qw = oracle_weights(layer_id, np.unique(ids[toks]))
     ref = oracle.moe_layer(x, ids, w, toks, H, I, qw, static_scales=(gx, ga))
     check_layer_tolerance(bf16_tensor_to_f64(out)[toks], ref)

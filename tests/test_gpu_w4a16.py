@@ -5,15 +5,17 @@ MFMA, weights dequantized exactly to bf16).
 
 Bit-exact: router ids and the permutation, and GEMM2's bf16 input against the
 bf16 rounding (the oracle's encoder) of the GPU's own SwiGLU output, on every
-expanded row.  Tolerance: the layer output as for the NVFP4 layer."""
+expanded row.  Tolerance: the layer output as for the NVFP4 layer, on every
+token, or for the prefill and large layers on the tokens covering every
+active expert's first and last expanded row (every tile shape)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from nvfp4_token_quant_amd import binding, synth
-from tests.layer_fixtures import (bf16_tensor_to_f64, check_layer_tolerance, gpu_weights,
-                                  oracle_expert, oracle_weights, to_device_bf16)
+from tests.layer_fixtures import (bf16_tensor_to_f64, check_layer_tolerance, covering_tokens,
+                                  gpu_weights, oracle_expert, oracle_weights, to_device_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +47,12 @@ def _check(layer_id, T, deterministic=True, shared=None, tokens=None, max_tokens
     if deterministic:
         np.testing.assert_array_equal(layer.read_buffer("PERM", torch.int32, (T * L.k,)).cpu().numpy(), perm)
     Rt = T * (L.k + (1 if shared else 0))
-    rows = np.arange(Rt) if Rt <= 8192 else np.arange(0, Rt, 37)
-    act = layer.read_buffer("ACT", torch.float32, (Rt, L.I)).cpu().numpy()[rows]
-    a16 = layer.read_buffer("A2_16", torch.int16, (Rt, L.I)).cpu().numpy().view(np.uint16)[rows]
+    act = layer.read_buffer("ACT", torch.float32, (Rt, L.I)).cpu().numpy()
+    a16 = layer.read_buffer("A2_16", torch.int16, (Rt, L.I)).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(a16, oracle.f32_to_bf16(act))
+    if isinstance(tokens, str):
+        tokens, present, covered = covering_tokens(oids, L.E)
+        assert present <= covered
     toks = np.arange(T) if tokens is None else tokens
     routed = oracle_weights(layer_id, np.unique(oids[toks]))
     if shared:
@@ -71,15 +75,16 @@ def test_w4a16_decode(T):
 
 
 @pytest.mark.timeout(900)
-def test_w4a16_prefill_sampled():
-    rng = np.random.default_rng(7)
-    _check(3, 4096, tokens=np.sort(rng.choice(4096, 32, replace=False)))
+def test_w4a16_prefill():
+    """Prefill-shaped layer: GEMM2's bf16 input on every row, the layer on
+    the tokens covering every expert's first and last expanded row."""
+    _check(3, 4096, tokens="covering")
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("T", [1, 7, 2048])
 def test_w4a16_large(T):
-    _check(5, T, tokens=None if T <= 7 else np.array([0, 999, T - 1]))
+    _check(5, T, tokens=None if T <= 7 else "covering")
 
 
 def test_w4a16_with_shared_expert():
