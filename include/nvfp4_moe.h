@@ -292,6 +292,31 @@ int moe_nvfp4_forward_quantized(moe_workspace* ws, const void* x_codes_dev, cons
                                 void* out_dev, void* stream);
 
 /*
+ * The forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It computes exactly what moe_nvfp4_forward computes for
+ * a workspace of configuration *cfg bound to *w (bit for bit with
+ * MOE_DETERMINISTIC_FINALIZE), with no allocation: every intermediate lives
+ * in one fixed 64 MiB device array inside the library, which each GPU the
+ * library runs on holds until the process ends.
+ *   cfg          dims and flags as for moe_workspace_create; T may not exceed
+ *                cfg->max_num_tokens (NVFP4_ERR_TOO_MANY_TOKENS).
+ *                MOE_STATIC_ACT_SCALES is not supported (NVFP4_ERR_INVALID_ARG)
+ *   w            packed weights (moe_pack_weights), read in place together
+ *                with its global-scale arrays for the call's duration
+ *   x_dev, logits_dev, T, out_dev, stream   as for moe_nvfp4_forward
+ * A forward whose intermediates exceed the array (for example more than
+ * about 600 tokens of a 2048 x 768 x 128-expert top-8 layer, about 180 of a
+ * 7168 x 2048 x 256-expert one) returns NVFP4_ERR_INVALID_ARG, naming the
+ * largest token count that fits, and launches nothing.  All calls on one GPU
+ * share that GPU's array, and it keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race.  The first call on
+ * each device looks the array's address up (make it outside graph capture).
+ */
+int moe_nvfp4_forward_noalloc(const moe_config* cfg, const moe_nvfp4_packed* w, const void* x_dev,
+                              const float* logits_dev, int64_t T, void* out_dev, void* stream);
+
+/*
  * Scale reload after a weight update ([P1] "Implementation breakdown" item 3
  * and "Source snippets", refresh_cutedsl_standard_scales_for_weight_update):
  * the new block scales are written INTO the bound packed records (the

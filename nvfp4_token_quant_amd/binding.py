@@ -98,6 +98,9 @@ def lib():
         L.moe_token_ceiling.argtypes = [_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
         L.moe_workspace_set_act_scales.restype = ctypes.c_int
         L.moe_workspace_set_act_scales.argtypes = [_P, _P, _P]
+        L.moe_nvfp4_forward_noalloc.restype = ctypes.c_int
+        L.moe_nvfp4_forward_noalloc.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoePacked), _P, _P,
+                                                _I64, _P, _P]
         L.moe_workspace_buffer.restype = ctypes.c_int
         L.moe_workspace_buffer.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(_I64)]
         _lib = L
@@ -416,6 +419,16 @@ class MoeLayer:
             self.close()
         except Exception:
             pass
+
+
+def forward_noalloc(cfg: MoeConfig, weights: PackedWeights, x, logits, out, T=None, stream=None):
+    """moe_nvfp4_forward_noalloc: the forward with no workspace and no
+    allocation (intermediates in the library's fixed device array)."""
+    T = x.shape[0] if T is None else T
+    d = weights.desc()
+    _check(lib().moe_nvfp4_forward_noalloc(ctypes.byref(cfg), ctypes.byref(d), _ptr(x), _ptr(logits), T,
+                                           _ptr(out), _stream(stream)))
+    return out
 
 
 _hip = None

@@ -23,7 +23,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I" + os.path.join(ROOT, "include")]
 
 LIBS = {
-    "libnvfp4moe.so": ["quantize.hip", "moe_kernels.hip", "gemm_kernels.hip", "moe_api.cpp"],
+    "libnvfp4moe.so": ["quantize.hip", "moe_kernels.hip", "gemm_kernels.hip", "moe_api.cpp", "noalloc.hip"],
     "libnvfp4synth.so": ["synth_weights.hip"],
 }
 
