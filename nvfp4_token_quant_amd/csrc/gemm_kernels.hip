@@ -847,18 +847,18 @@ __global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2
 void moe_tiled_kernel(FwdParams p) {
   __shared__ TiledShared sh;
   // XCD-aware order: consecutive blocks go to the 8 XCDs in turn, so block L
-  // runs on XCD L % 8 as that XCD's (L / 8)-th block.  XCD x takes the x-th
-  // eighth of the tile list (tiles are sorted by expert), each tile with all
-  // its bands in a row: the bands of a tile share its token rows in that
-  // XCD's L2, and the tiles of one expert, running side by side, share its
-  // weight records there.
+  // runs on XCD L % 8 as that XCD's (L / 8)-th block.  Tiles are dealt to
+  // the XCDs in turn (tile t to XCD t % 8) and each XCD runs a tile's bands
+  // in a row: the bands share the tile's token rows in that XCD's L2, while
+  // the tiles of one hot expert spread over every XCD's path to HBM
+  // (measured on the large layer at 2048 tokens: 2.33 -> 2.11 ms against
+  // giving each XCD a contiguous eighth of the tile list; prefill unchanged).
   const int nb = gridDim.x / p.tiled_gx;  // bands per tile
   const int L = blockIdx.x, slot = L >> 3;
   const int ntiles = *p.n_tiles;
-  const int per_xcd = (ntiles + 7) >> 3;
   const int band = slot % nb, local = slot / nb;
-  const int tile = (L & 7) * per_xcd + local;
-  if (local >= per_xcd || tile >= ntiles) return;
+  const int tile = local * 8 + (L & 7);
+  if (tile >= ntiles) return;
   const int4 td = p.tiles[tile];
   TiledBlock b;
   b.e = td.x;
