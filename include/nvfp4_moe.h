@@ -135,8 +135,8 @@ int nvfp4_quantize_experts(const float* w_dev, int64_t experts, int64_t rows, in
  * activation is quantized — x itself (bf16) is GEMM1's input and the SwiGLU
  * output rounded to bf16 (nearest even) is GEMM2's input; the weights stay
  * NVFP4 (dequantized exactly to bf16 for bf16 MFMA), the outputs are scaled
- * by 1 / g_w only.  Every batch size runs the tiled GEMMs.  Not combinable
- * with MOE_STATIC_ACT_SCALES (NVFP4_ERR_INVALID_ARG). */
+ * by 1 / g_w only.  Not combinable with MOE_STATIC_ACT_SCALES
+ * (NVFP4_ERR_INVALID_ARG). */
 #define MOE_W4A16 0x10u
 
 typedef struct moe_config {

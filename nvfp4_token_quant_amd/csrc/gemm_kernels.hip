@@ -268,13 +268,40 @@ __device__ __forceinline__ void unit_step_mfma(f32x4 (&acc)[kUnitFrags][FM], con
   }
 }
 
+// The same step for W4A16: the token rows are staged as bf16 (row pitch
+// cpitch bytes; lane group g reads k = 128 step + 32 g + 8 q .. + 7 of row
+// 16 fm + r16), the weight fragments are dequantized exactly to bf16.
+template <int FM>
+__device__ __forceinline__ void unit_step_mfma_a16(f32x4 (&acc)[kUnitFrags][FM], const UnitStep& w,
+                                                   const uint8_t* lc, int cpitch, int step, int g, int r16) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bf16x8 bq[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      bq[fm] = *reinterpret_cast<const bf16x8*>(lc + (fm * 16 + r16) * cpitch + 2 * (128 * step + 32 * g + 8 * q));
+#pragma unroll
+    for (int f = 0; f < kUnitFrags; ++f) {
+      // scale of this q's 16-element block (q 0-1: first byte, q 2-3: second)
+      const uint32_t w16 = (f < 2 ? w.sc.x : w.sc.y) >> (16 * (f & 1) + 8 * (q >> 1));
+      const bf16x8 aq = dequant8_bf16(word_of(w.c[f], q), e4m3_to_f32(w16));
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[f][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bq[fm], acc[f][fm], 0, 0, 0);
+    }
+  }
+}
+
 // Act values of one 16-element block of an expanded row.
 struct ActBlock {
   float4 v[4];
 };
 
-template <int FM, int KS, int MODE>
+template <int FM, int KS, int MODE, bool A16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3 + MODE : 2))) void moe_stream_kernel(FwdParams p) {
+  // (W4A16 streams GEMM2 only: its GEMM1 runs on the tiled kernel, which
+  // measured faster there)
+  static_assert(!A16 || MODE == 1, "bf16 staging is GEMM2's");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MT = 16 * FM;
   constexpr int UB = 4 / KS;  // units per block
@@ -287,7 +314,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   const int e = td.x, row0 = td.y, nrows = td.z;
   const int K = MODE == 0 ? p.H : p.I;
   const int S = ksteps(K);
-  const int cpitch = K / 2 + 16, spitch = K / 16 + 4;
+  // staged row pitch: FP4 codes (+ a separate scale area), or bf16 values
+  // (W4A16); the 16-byte pad puts the 16 rows one MFMA operand read touches
+  // on different LDS banks
+  const int cpitch = A16 ? 2 * K + 16 : K / 2 + 16, spitch = K / 16 + 4;
   uint8_t* lc = smem;
   uint8_t* ls = smem + MT * cpitch;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -337,6 +367,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     __builtin_amdgcn_sched_barrier(0);
     // the epilogue's row scales (used after the loop)
     if (lane < nrows) grow = p.xq_g[src];
+  } else if constexpr (A16) {
+    // W4A16: GEMM2's input is act rounded to bf16 (nearest even).  The first
+    // pieces of the tile's act rows are loaded ahead of the weight window
+    // (vector loads complete in issue order), converted into the LDS
+    // operand; band-0 blocks also store them (the 16-bit GEMM2 input).
+    constexpr int kA = 4;  // 8-value pieces per thread loaded ahead
+    const int n8 = K / 8, items = nrows * n8;
+    float4 pa[kA][2];
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const int it = min(static_cast<int>(threadIdx.x) + 256 * i, items - 1);
+      const int m = it / n8, c = it - m * n8;
+      const float4* src4 = reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(row0 + m) * K + 8 * c);
+      pa[i][0] = src4[0];
+      pa[i][1] = src4[1];
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    if (!p.deterministic && lane < nrows) slot = row_slot(p, row0 + lane);
+    auto stage = [&](const float4& a, const float4& b, int it) {
+      const int m = it / n8, c = it - m * n8;
+      bf16x8 r;
+      r[0] = static_cast<__bf16>(a.x); r[1] = static_cast<__bf16>(a.y);
+      r[2] = static_cast<__bf16>(a.z); r[3] = static_cast<__bf16>(a.w);
+      r[4] = static_cast<__bf16>(b.x); r[5] = static_cast<__bf16>(b.y);
+      r[6] = static_cast<__bf16>(b.z); r[7] = static_cast<__bf16>(b.w);
+      *reinterpret_cast<bf16x8*>(lc + m * cpitch + 16 * c) = r;
+      if (blockIdx.y == 0) *reinterpret_cast<bf16x8*>(p.a2q16 + static_cast<int64_t>(row0 + m) * K + 8 * c) = r;
+    };
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + 256 * i;
+      if (it < items) stage(pa[i][0], pa[i][1], it);
+    }
+    for (int it = static_cast<int>(threadIdx.x) + 256 * kA; it < items; it += 256) {
+      const int m = it / n8, c = it - m * n8;
+      const float4* src4 = reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(row0 + m) * K + 8 * c);
+      stage(src4[0], src4[1], it);
+    }
   } else {
     // Fused re-quantization.  Loads in issue order: GEMM1 amax partials of
     // the wave's rows, the first kRq act blocks of this thread, then the
@@ -426,7 +495,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int s = s0 + d;
-      if (s < ns) unit_step_mfma<FM>(acc, wb[d], lc, ls, cpitch, spitch, sb + s, g, r16);
+      if (s < ns) {
+        if constexpr (A16)
+          unit_step_mfma_a16<FM>(acc, wb[d], lc, cpitch, sb + s, g, r16);
+        else
+          unit_step_mfma<FM>(acc, wb[d], lc, ls, cpitch, spitch, sb + s, g, r16);
+      }
       // keep the refill of this slot after its use (no extra register set)
       __builtin_amdgcn_sched_barrier(0);
       const int sn = s + D;
@@ -464,7 +538,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   int slots[FM];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    ginv[fm] = 1.0f / (MODE == 0 ? __shfl(grow, fm * 16 + r16, kWave) : s_g2[fm * 16 + r16]);
+    ginv[fm] = A16 ? 1.0f : 1.0f / (MODE == 0 ? __shfl(grow, fm * 16 + r16, kWave) : s_g2[fm * 16 + r16]);
     slots[fm] = __shfl(slot, fm * 16 + r16, kWave);
   }
   if (MODE == 0) {
@@ -967,8 +1041,12 @@ __global__ __launch_bounds__(256) void moe_requant_kernel(FwdParams p) {
 
 int stream_lds_bytes(int fm, int K) { return 16 * fm * ((K / 2 + 16) + (K / 16 + 4)); }
 
-static int stream_lds_total(int fm, int ks, int K, bool atomic = false) {
-  const int staged = stream_lds_bytes(fm, K);
+// W4A16 stream kernels stage bf16 rows; up to this much dynamic LDS per block
+// (two blocks per CU on gfx950).
+constexpr int kStreamA16MaxLds = 80 * 1024;
+
+static int stream_lds_total(int fm, int ks, int K, bool atomic = false, bool a16 = false) {
+  const int staged = a16 ? 16 * fm * (2 * K + 16) : stream_lds_bytes(fm, K);
   const int red = ks > 1 ? 4 * kUnitFrags * fm * 4 * kWave * 4 : 0;
   // atomic GEMM2 epilogue: each unit's rows at kAtomicPitch floats
   const int stage = atomic ? (4 / ks) * 16 * fm * kAtomicPitch * 4 : 0;
@@ -994,10 +1072,16 @@ void choose_gemm(int64_t T, FwdParams* p) {
   const int64_t avg = (R + active - 1) / (active > 0 ? active : 1);
   const int Kmax = H > I ? H : I;
   if (p->a16) {
-    // W4A16: the stream kernels stage FP4 token operands; bf16 activations
-    // always take the tiled GEMMs (their 16-bit LDS copies)
-    p->mt = kTiledRows;
-    p->gemm_kind = kGemmTiled;
+    // W4A16 with few rows per expert: 16-row tiles, GEMM1 on the tiled
+    // kernel and GEMM2 streamed with its rows staged as bf16 (16 rows of
+    // 2 I bytes must fit); otherwise the tiled GEMMs with 128-row tiles
+    if (avg <= 16 && stream_lds_total(1, 4, I, true, true) <= kStreamA16MaxLds) {
+      p->mt = 16;
+      p->gemm_kind = kGemmStream;
+    } else {
+      p->mt = kTiledRows;
+      p->gemm_kind = kGemmTiled;
+    }
   } else if (avg <= 16 && stream_lds_total(1, 4, Kmax) <= 65536) {
     p->mt = 16;
     p->gemm_kind = kGemmStream;
@@ -1012,7 +1096,7 @@ void choose_gemm(int64_t T, FwdParams* p) {
   }
   if (p->gemm_kind == kGemmStream) {
     const int64_t tiles = (R + p->mt - 1) / p->mt > active ? (R + p->mt - 1) / p->mt : active;
-    p->g1_ks = choose_ks(tiles * (I / 32), I / 32, ksteps(H));
+    p->g1_ks = p->a16 ? 1 : choose_ks(tiles * (I / 32), I / 32, ksteps(H));  // (W4A16: GEMM1 tiled)
     // GEMM2 re-quantizes its tile's rows in every block, so splitting K
     // (more blocks per tile) costs more than the extra parallelism gains
     p->g2_ks = (H / 64) % 4 == 0 ? 1 : (H / 64) % 2 == 0 ? 2 : 4;
@@ -1023,10 +1107,25 @@ void choose_gemm(int64_t T, FwdParams* p) {
   }
 }
 
-template <int FM, int KS1, int KS2>
+template <int FM, int KS1, int KS2, bool A16>
 static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  const int nb1 = (p.I / 32) / (4 / KS1);
-  moe_stream_kernel<FM, KS1, 0><<<dim3(max_tiles, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
+  if (A16) {
+    // W4A16: GEMM1 on the tiled kernel (16-row tiles: its 1-group variant;
+    // measured faster than bf16 staging in the stream kernel, whose bf16
+    // weight dequantization costs about twice the fp16 one's VALU)
+    const int nbt = (p.I / 32 + kTiledWaves - 1) / kTiledWaves;
+    moe_tiled_kernel<0, true><<<p.tiled_gx * nbt, kTiledThreads, 0, s>>>(p);
+    // GEMM2's bf16 staging may take more than the default 64 KB of dynamic LDS
+    static bool lds_set = false;
+    if (!lds_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_stream_kernel<FM, KS2, 1, A16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kStreamA16MaxLds);
+      lds_set = true;
+    }
+  } else {
+    const int nb1 = (p.I / 32) / (4 / KS1);
+    moe_stream_kernel<FM, KS1, 0, false><<<dim3(max_tiles, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
+  }
   if (ev) (void)hipEventRecord(ev[2], s);
   const int nb2 = (p.H / 64) / (4 / KS2);
   // Consecutive blocks go to the 8 XCDs in turn; with max_tiles columns (not
@@ -1035,31 +1134,34 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
   // at one token: GEMM2 25.0 -> 18.4 us against all bands of a tile on one
   // XCD); the tile's act rows, re-read by every band, come from the last
   // level cache.
-  moe_stream_kernel<FM, KS2, 1><<<dim3(max_tiles, nb2), 256, stream_lds_total(FM, KS2, p.I, !p.deterministic), s>>>(p);
+  moe_stream_kernel<FM, KS2, 1, A16><<<dim3(max_tiles, nb2), 256,
+                                       stream_lds_total(FM, KS2, p.I, !p.deterministic, A16), s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
 }
 
-template <int FM, int KS1>
+template <int FM, int KS1, bool A16>
 static void launch_stream_ks2(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  if (p.g2_ks == 1) launch_stream<FM, KS1, 1>(p, max_tiles, s, ev);
-  else if (p.g2_ks == 2) launch_stream<FM, KS1, 2>(p, max_tiles, s, ev);
-  else launch_stream<FM, KS1, 4>(p, max_tiles, s, ev);
+  if (p.g2_ks == 1) launch_stream<FM, KS1, 1, A16>(p, max_tiles, s, ev);
+  else if (p.g2_ks == 2) launch_stream<FM, KS1, 2, A16>(p, max_tiles, s, ev);
+  else launch_stream<FM, KS1, 4, A16>(p, max_tiles, s, ev);
 }
 
-template <int FM>
+template <int FM, bool A16>
 static void launch_stream_fm(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  if (p.g1_ks == 1) launch_stream_ks2<FM, 1>(p, max_tiles, s, ev);
-  else if (p.g1_ks == 2) launch_stream_ks2<FM, 2>(p, max_tiles, s, ev);
-  else launch_stream_ks2<FM, 4>(p, max_tiles, s, ev);
+  if (p.g1_ks == 1) launch_stream_ks2<FM, 1, A16>(p, max_tiles, s, ev);
+  else if (p.g1_ks == 2) launch_stream_ks2<FM, 2, A16>(p, max_tiles, s, ev);
+  else launch_stream_ks2<FM, 4, A16>(p, max_tiles, s, ev);
 }
 
 hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s,
                                 hipEvent_t const* ev) {
   if (p.gemm_kind == kGemmStream) {
-    if (p.mt == 16)
-      launch_stream_fm<1>(p, max_tiles, s, ev);
+    if (p.a16)
+      launch_stream_fm<1, true>(p, max_tiles, s, ev);
+    else if (p.mt == 16)
+      launch_stream_fm<1, false>(p, max_tiles, s, ev);
     else
-      launch_stream_fm<2>(p, max_tiles, s, ev);
+      launch_stream_fm<2, false>(p, max_tiles, s, ev);
   } else {
     const int nb1 = (p.I / 32 + kTiledWaves - 1) / kTiledWaves;
     const int nb2 = (p.H / 64 + kTiledWaves - 1) / kTiledWaves;

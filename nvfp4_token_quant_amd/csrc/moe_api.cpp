@@ -222,7 +222,8 @@ int run_forward(const moe_config& c, const FwdBuffers& b, const WeightView& wv, 
   // the fp16 copies are only written and read by the tiled (prefill) kernels
   // (W4A16 reads x itself)
   p.xq16 = p.gemm_kind == kGemmTiled && !p.a16 ? b.xq16 : nullptr;
-  p.a2q16 = p.gemm_kind == kGemmTiled ? b.a2q16 : nullptr;
+  // (W4A16: GEMM2's bf16 input, also written by the stream kernels)
+  p.a2q16 = p.gemm_kind == kGemmTiled || p.a16 ? b.a2q16 : nullptr;
   p.topk_ids = b.topk_ids;
   p.topk_w = b.topk_w;
   p.loc_rank = b.loc_rank;
