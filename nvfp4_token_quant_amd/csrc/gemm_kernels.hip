@@ -138,7 +138,9 @@ __device__ __forceinline__ uint32_t requant_block(const float* __restrict__ src,
 
 // GEMM2: per lane, fragment f holds y[n = n0 + 16 f + 4g + i] of row m =
 // 16 fm + r16; ginv[fm] = 1 / (that row's a2 global scale), slot[fm] = its
-// t*k+j (atomic finalize only), wginv = 1 / (the expert's W2 global scale).
+// t*k+j, wginv = 1 / (the expert's W2 global scale).  y is stored by slot
+// (row t*k+j of y is token t's j-th expert output), so the finalize reads
+// each token's k rows contiguously, without the inverse permutation.
 template <int FM, int FN>
 __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&acc)[FN][FM], int e,
                                             int row0, int nrows, int n0, const float (&ginv)[FM],
@@ -149,14 +151,13 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
     const int m = fm * 16 + r16;
     if (m >= nrows) continue;
     const float alpha = ginv[fm] * wginv;
-    const int64_t row = row0 + m;
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       const int n = n0 + f * 16 + 4 * g;
       const float y0 = acc[f][fm][0] * alpha, y1 = acc[f][fm][1] * alpha;
       const float y2 = acc[f][fm][2] * alpha, y3 = acc[f][fm][3] * alpha;
       if (p.deterministic) {
-        *reinterpret_cast<float4*>(p.y + row * H + n) = make_float4(y0, y1, y2, y3);
+        *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(slot[fm]) * H + n) = make_float4(y0, y1, y2, y3);
       } else {
         const float w = slot_weight(p, slot[fm]);
         float* dst = p.out_acc + static_cast<int64_t>(slot_token(p, slot[fm])) * H + n;
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-    if (!p.deterministic && lane < nrows) slot = row_slot(p, row0 + lane);
+    if (lane < nrows) slot = row_slot(p, row0 + lane);
     auto stage = [&](const float4& a, const float4& b, int it) {
       const int m = it / n8, c = it - m * n8;
       bf16x8 r;
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
-    if (!p.deterministic && lane < nrows) slot = row_slot(p, row0 + lane);
+    if (lane < nrows) slot = row_slot(p, row0 + lane);
     // row global scales g2 = 2688 / amax(act row)
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -816,7 +817,8 @@ __device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared&
         const int m = 4 * i + (lane >> 4);
         if (m < nr) {
           const float4 v = *reinterpret_cast<const float4*>(st + m * kAtomicPitch + 4 * (lane & 15));
-          *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(row0 + 16 * r + m) * H + n0 + 4 * (lane & 15)) = v;
+          // y by slot (see g2_epilogue)
+          *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(sh.slot[16 * r + m]) * H + n0 + 4 * (lane & 15)) = v;
         }
       }
     } else {

@@ -655,13 +655,14 @@ static void launch_prologue_small(const FwdParams& p, hipStream_t s) {
   else moe_prologue_small_kernel<NB, 16><<<blocks, kSmallThreads, 0, s>>>(p);
 }
 
-// Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[inv[t, j], n]) in slot
-// order (deterministic), or bf16_rne(out_acc[t, n]) after the atomic epilogue.
+// Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[t * k + j, n]) in slot
+// order (deterministic; GEMM2 stores y by slot), or bf16_rne(out_acc[t, n])
+// after the atomic epilogue.
 // With a shared expert the deterministic sum adds its row R + t last and the
 // total is multiplied by the combination scale (1 or 0.5, exact); the atomic
 // epilogue applies the scale to each contribution.
 // One thread per 4 output columns; the slots are taken 8 at a time with all
-// their row-index, weight and y loads issued before the sums.
+// their weight and y loads issued before the sums.
 __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
   const int H = p.H, k = p.k;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -672,17 +673,15 @@ __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.deterministic) {
     for (int j0 = 0; j0 < k; j0 += 8) {
-      int rows[8];
       float w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t sl = t * k + min(j0 + j, k - 1);
-        rows[j] = p.inv[sl];
-        w[j] = j0 + j < k ? p.topk_w[sl] : 0.0f;
-      }
       float4 y[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = *reinterpret_cast<const float4*>(p.y + static_cast<int64_t>(rows[j]) * H + n);
+      for (int j = 0; j < 8; ++j) {
+        // GEMM2 stored y by slot: token t's rows are t*k .. t*k + k - 1
+        const int64_t sl = t * k + min(j0 + j, k - 1);
+        w[j] = j0 + j < k ? p.topk_w[sl] : 0.0f;
+        y[j] = *reinterpret_cast<const float4*>(p.y + sl * H + n);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j0 + j < k) {
