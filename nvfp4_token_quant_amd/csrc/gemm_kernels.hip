@@ -746,16 +746,20 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Shared memory of one tiled block (sized for the largest tile).
+// Shared memory of one tiled block, sized for tiles of up to TR rows.
+template <int TR>
 struct TiledShared {
-  uint8_t lds[2][kTiledRows * 256] __attribute__((aligned(16)));
-  int src[kTiledRows];
-  int slot[kTiledRows];
-  float ginv[kTiledRows];
+  uint8_t lds[2][TR * 256] __attribute__((aligned(16)));
+  int src[TR];
+  int slot[TR];
+  float ginv[TR];
   float wginv;  // 1 / (the expert's weight global scale)
-  float amax[kTiledWaves][kTiledRows];
+  float amax[kTiledWaves][TR];
 };
-static_assert(sizeof(TiledShared) <= 80 * 1024, "two tiled blocks must share a CU's LDS");
+static_assert(sizeof(TiledShared<kTiledRows>) <= 80 * 1024, "two tiled blocks must share a CU's LDS");
+// Tiles of at most 16 rows (16-row tiles of decode-sized W4A16 batches): the
+// block's LDS and registers are small enough for four blocks per CU.
+constexpr int kTiledSmallRows = 16;
 
 // What a tiled block works on.
 struct TiledBlock {
@@ -774,11 +778,12 @@ struct TiledBlock {
 // instruction, an atomic (w * y into out_acc) one whole row segment.
 // Called by every wave of the block (barriers).
 template <int FMV>
-__device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared& sh,
+__device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared<kTiledRows>& sh,
                                                 const f32x4 (&acc)[kUnitFrags][FMV], int row0, int nrows,
                                                 int n0, const float (&ginv)[FMV], float wginv, bool has_unit,
                                                 int wave, int lane) {
-  static_assert(kTiledWaves * 32 * kAtomicPitch * 4 <= sizeof(TiledShared::lds), "staging fits the token buffers");
+  static_assert(kTiledWaves * 32 * kAtomicPitch * 4 <= sizeof(TiledShared<kTiledRows>::lds),
+                "staging fits the token buffers");
   const int t = threadIdx.x, g = lane >> 4, r16 = lane & 15;
   wait_vmcnt<0>();  // this wave's last copies have landed
   // every wave is done with the token buffers; for the atomics each row's
@@ -835,9 +840,11 @@ __device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared&
 // epilogue cover only those groups, so a tile of few rows costs in
 // proportion to its rows (FMV is the smallest of 1, 2, 3, 4, 6, 8 groups
 // that holds them).
-template <int FMV, int MODE, bool A16>
-__device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, const TiledBlock& b,
+template <int FMV, int MODE, bool A16, int TR>
+__device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared<TR>& sh, const TiledBlock& b,
                                            UnitStep (&wb)[2], float my_g, int my_slot, float wg) {
+  static_assert(16 * FMV <= TR, "the tile's groups fit the block's buffers");
+  static_assert(MODE == 0 || TR == kTiledRows, "GEMM2's epilogue stages through the 128-row buffers");
   constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
   const int row0 = b.row0, nrows = b.nrows, K = b.K, S = b.S, j = b.j;
   const bool has_unit = b.has_unit;
@@ -874,7 +881,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
   // stores visible).  The weight records of the first two steps were issued
   // before everything else; the K loop's waits count one refill newer than
   // the step's copies, so wait here for all of it, the first copies included.
-  if (t < kTiledRows) {
+  if (t < TR) {
     sh.ginv[t] = t < nrows ? 1.0f / my_g : 0.0f;
     sh.slot[t] = my_slot;
   }
@@ -905,23 +912,26 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared& sh, 
     ginv[fm] = sh.ginv[fm * 16 + r16];
     slots[fm] = sh.slot[fm * 16 + r16];
   }
-  if (MODE == 0) {
+  if constexpr (MODE == 0) {
     if (has_unit) {
-      g1_epilogue<FMV, 2, kTiledRows>(p, acc, b.e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16, wginv);
+      g1_epilogue<FMV, 2, TR>(p, acc, b.e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16, wginv);
     } else if (g == 0) {
 #pragma unroll
       for (int fm = 0; fm < FMV; ++fm) sh.amax[wave][fm * 16 + r16] = 0.0f;
     }
-    g1_store_band_amax<kTiledRows>(p, sh.amax, row0, nrows, b.band, b.nb);
+    g1_store_band_amax<TR>(p, sh.amax, row0, nrows, b.band, b.nb);
   } else {
     tiled_g2_staged<FMV>(p, sh, acc, row0, nrows, 64 * j, ginv, wginv, has_unit, wave, lane);
   }
 }
 
-template <int MODE, bool A16>
-__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// TR: the most rows a tile of this launch has (kTiledRows, or kTiledSmallRows
+// when the tile list was built with 16-row tiles: two blocks per CU, or four).
+template <int MODE, bool A16, int TR = kTiledRows>
+__global__ __launch_bounds__(kTiledThreads)
+__attribute__((amdgpu_waves_per_eu(TR == kTiledSmallRows ? 4 : 2, TR == kTiledSmallRows ? 4 : 2)))
 void moe_tiled_kernel(FwdParams p) {
-  __shared__ TiledShared sh;
+  __shared__ TiledShared<TR> sh;
   // XCD-aware order: consecutive blocks go to the 8 XCDs in turn, so block L
   // runs on XCD L % 8 as that XCD's (L / 8)-th block.  Tiles are dealt to
   // the XCDs in turn (tile t to XCD t % 8) and each XCD runs a tile's bands
@@ -969,26 +979,30 @@ void moe_tiled_kernel(FwdParams p) {
       src = slot_token(p, my_slot);
       if (!A16) my_g = p.xq_g[src];
     }
-    if (t < kTiledRows) sh.src[t] = src;
+    if (t < TR) sh.src[t] = src;
     lds_barrier();
   } else if (t < b.nrows) {
     if (!A16) my_g = p.a2_g[b.row0 + t];
     my_slot = row_slot(p, b.row0 + t);
   }
   const float wg = MODE == 0 ? p.w13g[b.e] : p.w2g[b.e];
-  const int groups = (b.nrows + 15) >> 4;
-  if (groups > 6)
-    tiled_tile<8, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
-  else if (groups > 4)
-    tiled_tile<6, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
-  else if (groups > 3)
-    tiled_tile<4, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
-  else if (groups > 2)
-    tiled_tile<3, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
-  else if (groups > 1)
-    tiled_tile<2, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
-  else
-    tiled_tile<1, MODE, A16>(p, sh, b, wb, my_g, my_slot, wg);
+  if constexpr (TR == kTiledSmallRows) {
+    tiled_tile<1, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+  } else {
+    const int groups = (b.nrows + 15) >> 4;
+    if (groups > 6)
+      tiled_tile<8, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+    else if (groups > 4)
+      tiled_tile<6, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+    else if (groups > 3)
+      tiled_tile<4, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+    else if (groups > 2)
+      tiled_tile<3, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+    else if (groups > 1)
+      tiled_tile<2, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+    else
+      tiled_tile<1, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1111,12 +1125,14 @@ void choose_gemm(int64_t T, FwdParams* p) {
 
 template <int FM, int KS1, int KS2, bool A16>
 static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipEvent_t const* ev) {
-  if (A16) {
-    // W4A16: GEMM1 on the tiled kernel (16-row tiles: its 1-group variant;
-    // measured faster than bf16 staging in the stream kernel, whose bf16
-    // weight dequantization costs about twice the fp16 one's VALU)
+  if constexpr (A16) {
+    // W4A16: GEMM1 on the tiled kernel (16-row tiles: its 1-group variant,
+    // sized for them, four blocks per CU; measured faster than bf16 staging
+    // in the stream kernel, whose bf16 weight dequantization costs about
+    // twice the fp16 one's VALU)
+    static_assert(FM * 16 <= kTiledSmallRows, "the stream path's tiles fit the small tiled blocks");
     const int nbt = (p.I / 32 + kTiledWaves - 1) / kTiledWaves;
-    moe_tiled_kernel<0, true><<<p.tiled_gx * nbt, kTiledThreads, 0, s>>>(p);
+    moe_tiled_kernel<0, true, kTiledSmallRows><<<p.tiled_gx * nbt, kTiledThreads, 0, s>>>(p);
     // GEMM2's bf16 staging may take more than the default 64 KB of dynamic LDS
     static bool lds_set = false;
     if (!lds_set) {
