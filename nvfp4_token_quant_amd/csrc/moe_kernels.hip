@@ -332,6 +332,35 @@ constexpr int kSmallMaxT = 256, kSmallMaxE = 256, kSmallMaxR = 2048;
 constexpr int kSmallThreads = 1024;  // 16 waves: 64 tokens routed per pass
 constexpr int kSmallWaves = kSmallThreads / 64;
 
+// Router for one token by a 16-lane group (lane gl of the group holds
+// experts gl, gl + 16, ...): lane j < k of the group ends with the j-th
+// chosen expert and its weight.  Each lane first sorts its KPL keys (largest
+// first) with Batcher's odd-even merge sorting network (K. E. Batcher,
+// "Sorting networks and their applications", AFIPS 1968), so that each of
+// the k selection rounds only takes the row maximum of the lanes' heads and
+// pops the winning lane's list, instead of rescanning all KPL keys of every
+// lane per round.  Keys are unique (the expert index is part of them), so the
+// selection is the same either way.
+__device__ __forceinline__ void key_cx(uint64_t& a, uint64_t& b) {
+  const bool sw = b > a;
+  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+
+template <int N>
+__device__ __forceinline__ void sort_keys_desc(uint64_t (&c)[N]) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+    for (int d = p; d >= 1; d >>= 1)
+#pragma unroll
+      for (int j = d % p; j + d < N; j += 2 * d)
+#pragma unroll
+        for (int i = 0; i < d; ++i)
+          if (i + j + d < N && (i + j) / (2 * p) == (i + j + d) / (2 * p)) key_cx(c[i + j], c[i + j + d]);
+}
+
 template <int KPL>
 __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k, int gl,
                                     int& my_id, float& my_w) {
@@ -346,16 +375,18 @@ __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k
     const int e = gl + 16 * i;
     cand[i] = e < E ? route_key(v[i], e) : 0ull;
   }
+  sort_keys_desc<KPL>(cand);
   uint64_t mine = 0, top = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) best = cand[i] > best ? cand[i] : best;
-    best = row16_max(best);
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
-    if (gl == j) mine = best;
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    const uint64_t best = row16_max(cand[0]);
     if (j == 0) top = best;
+    mine = gl == j ? best : mine;
+    const bool pop = cand[0] == best;  // this lane held the winner
+#pragma unroll
+    for (int i = 0; i + 1 < KPL; ++i) cand[i] = pop ? cand[i + 1] : cand[i];
+    cand[KPL - 1] = pop ? 0ull : cand[KPL - 1];
   }
   const float ex = gl < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
   const float sum = row16_sum(ex);
