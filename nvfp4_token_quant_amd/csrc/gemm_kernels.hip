@@ -409,9 +409,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
     }
   } else {
     // Fused re-quantization.  Loads in issue order: GEMM1 amax partials of
-    // the wave's rows, the first kRq act blocks of this thread, then the
-    // whole weight prefetch window; each wait below covers only the loads
-    // it needs.
+    // the wave's rows, the first kRq act blocks of this thread, the first
+    // weight record; the rest of the prefetch window goes out once the
+    // operand is staged (with the whole window issued first, GEMM2 took
+    // 0.8-0.9 us longer at T=64 on the decode-shaped layer and at T=1 on the
+    // large layer).  Each wait below covers only the loads it
+    // needs.
     const int nbl = K / 16, nb = p.g1_bands;
     const int items = nrows * nbl;
     constexpr int RPW = MT / 4;  // rows per wave
@@ -431,8 +434,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
 #pragma unroll
       for (int q = 0; q < 4; ++q) ab[i].v[q] = src4[q];
     }
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
+    load_unit_step(wb[0], 0 < ns ? rec : p.dummy, lane);
     if (lane < nrows) slot = row_slot(p, row0 + lane);
     // row global scales g2 = 2688 / amax(act row)
 #pragma unroll
@@ -483,6 +485,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
         quant_item(a, it);
       }
     }
+#pragma unroll
+    for (int d = 1; d < D; ++d) load_unit_step(wb[d], d < ns ? rec + d * kRecBytes : p.dummy, lane);
   }
 
   f32x4 acc[kUnitFrags][FM];
