@@ -197,10 +197,16 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
 //   (see launch_stream): spreading each expert's weight stream over the
 //   XCDs matters more than keeping the repeated act reads in one L2.
 // ---------------------------------------------------------------------------
-template <int MODE>
+// Weight records each wave keeps in flight.  GEMM2 with a short K range
+// (SHORT: at most kStreamShortSteps K steps, e.g. I = 768) keeps 2: measured
+// on the decode-shaped layer at T=64 (6 steps per unit), GEMM2 26.2-26.5 ->
+// 25.3-25.7 us against 3, while with 16 steps (the large layer, I = 2048) 2
+// records were slower (T=1 17.9 -> 19.9 us, T=7 52 -> 57 us).
+template <int MODE, bool SHORT = false>
 struct StreamDepth {
-  static constexpr int value = MODE == 0 ? 5 : 3;
+  static constexpr int value = MODE == 0 ? 5 : (SHORT ? 2 : 3);
 };
+constexpr int kStreamShortSteps = 8;
 constexpr int kStreamEarly = 2;  // steps issued before the staging copies
 
 // Copy `bytes` bytes from global memory to LDS with global_load_lds: one wave
@@ -298,7 +304,7 @@ struct ActBlock {
   float4 v[4];
 };
 
-template <int FM, int KS, int MODE, bool A16>
+template <int FM, int KS, int MODE, bool A16, bool SHORT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3 + MODE : 2))) void moe_stream_kernel(FwdParams p) {
   // (W4A16 streams GEMM2 only: its GEMM1 runs on the tiled kernel, which
   // measured faster there)
@@ -306,7 +312,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MT = 16 * FM;
   constexpr int UB = 4 / KS;  // units per block
-  constexpr int D = StreamDepth<MODE>::value;
+  static_assert(!SHORT || (MODE == 1 && !A16), "the short window is NVFP4 GEMM2's");
+  constexpr int D = StreamDepth<MODE, SHORT>::value;
   constexpr int kRq = 2;  // re-quantization items per thread loaded ahead of the weights
   __shared__ float s_amax[4][MT];
   __shared__ float s_g2[MT];
@@ -1156,8 +1163,11 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
   // at one token: GEMM2 25.0 -> 18.4 us against all bands of a tile on one
   // XCD); the tile's act rows, re-read by every band, come from the last
   // level cache.
-  moe_stream_kernel<FM, KS2, 1, A16><<<dim3(max_tiles, nb2), 256,
-                                       stream_lds_total(FM, KS2, p.I, !p.deterministic, A16), s>>>(p);
+  const int lds2 = stream_lds_total(FM, KS2, p.I, !p.deterministic, A16);
+  if (!A16 && KS2 == 1 && ksteps(p.I) <= kStreamShortSteps)
+    moe_stream_kernel<FM, KS2, 1, false, true><<<dim3(max_tiles, nb2), 256, lds2, s>>>(p);
+  else
+    moe_stream_kernel<FM, KS2, 1, A16><<<dim3(max_tiles, nb2), 256, lds2, s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
 }
 
