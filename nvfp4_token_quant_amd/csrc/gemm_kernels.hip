@@ -200,8 +200,9 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
 // Weight records each wave keeps in flight.  GEMM2 with a short K range
 // (SHORT: at most kStreamShortSteps K steps, e.g. I = 768) keeps 2: measured
 // on the decode-shaped layer at T=64 (6 steps per unit), GEMM2 26.2-26.5 ->
-// 25.3-25.7 us against 3, while with 16 steps (the large layer, I = 2048) 2
-// records were slower (T=1 17.9 -> 19.9 us, T=7 52 -> 57 us).
+// 25.3-25.7 us against 3 (W4A16: 28.3-28.7 -> 27.4-27.6 us), while with 16
+// steps (the large layer, I = 2048) 2 records were slower (T=1 17.9 -> 19.9
+// us, T=7 52 -> 57 us).
 template <int MODE, bool SHORT = false>
 struct StreamDepth {
   static constexpr int value = MODE == 0 ? 5 : (SHORT ? 2 : 3);
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 1 ? 3
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MT = 16 * FM;
   constexpr int UB = 4 / KS;  // units per block
-  static_assert(!SHORT || (MODE == 1 && !A16), "the short window is NVFP4 GEMM2's");
+  static_assert(!SHORT || MODE == 1, "the short window is GEMM2's");
   constexpr int D = StreamDepth<MODE, SHORT>::value;
   constexpr int kRq = 2;  // re-quantization items per thread loaded ahead of the weights
   __shared__ float s_amax[4][MT];
@@ -1149,6 +1150,8 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
     if (!lds_set) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_stream_kernel<FM, KS2, 1, A16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kStreamA16MaxLds);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_stream_kernel<FM, KS2, 1, A16, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kStreamA16MaxLds);
       lds_set = true;
     }
   } else {
@@ -1164,8 +1167,8 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
   // XCD); the tile's act rows, re-read by every band, come from the last
   // level cache.
   const int lds2 = stream_lds_total(FM, KS2, p.I, !p.deterministic, A16);
-  if (!A16 && KS2 == 1 && ksteps(p.I) <= kStreamShortSteps)
-    moe_stream_kernel<FM, KS2, 1, false, true><<<dim3(max_tiles, nb2), 256, lds2, s>>>(p);
+  if (KS2 == 1 && ksteps(p.I) <= kStreamShortSteps)
+    moe_stream_kernel<FM, KS2, 1, A16, true><<<dim3(max_tiles, nb2), 256, lds2, s>>>(p);
   else
     moe_stream_kernel<FM, KS2, 1, A16><<<dim3(max_tiles, nb2), 256, lds2, s>>>(p);
   if (ev) (void)hipEventRecord(ev[3], s);
