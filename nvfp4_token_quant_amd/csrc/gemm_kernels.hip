@@ -232,9 +232,19 @@ struct UnitStep {
   uint4 c[kUnitFrags];
   uint2 sc;
 };
+// NT: non-temporal code loads, for kernels that read each record once (the
+// stream kernels; the tiled kernel's 16-row variant).  The 128-row tiled
+// kernels read an expert's records again for each of its tiles and load them
+// cached (measured: prefill-shaped layer 465-467 -> 440-441 us, GEMM1
+// 236-242 -> 218-223 us, GEMM2 187-189 -> 174-177 us; large layer at
+// T=2048 2.195 -> 2.078 ms; the decode-shaped layer's stream GEMMs were
+// 4-5 us slower with cached loads, W4A16 decode's 16-row tiled GEMM1 3 us).
+template <bool NT = true>
 __device__ __forceinline__ void load_unit_step(UnitStep& u, const uint8_t* rec, int lane) {
 #pragma unroll
-  for (int f = 0; f < kUnitFrags; ++f) u.c[f] = load_stream16(rec + 1024 * f + 16 * lane);
+  for (int f = 0; f < kUnitFrags; ++f)
+    u.c[f] = NT ? load_stream16(rec + 1024 * f + 16 * lane)
+                : *reinterpret_cast<const uint4*>(rec + 1024 * f + 16 * lane);
   u.sc = *reinterpret_cast<const uint2*>(rec + kRecCodeBytes + 8 * lane);
 }
 
@@ -684,7 +694,8 @@ __device__ __forceinline__ void tiled_copy_step(__amdgpu_buffer_rsrc_t rs, const
 // One K step: wait for this step's copies, start the next step's, MFMAs on
 // the LDS operand `cur` and the weight record in `w`, then refill `w` with
 // the record two steps ahead.
-template <int FM, int NCP, bool A16>
+// NT: the weight records are loaded non-temporally (see load_unit_step).
+template <int FM, int NCP, bool A16, bool NT>
 __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, int S, const uint8_t* cur,
                                            uint8_t* nxt, UnitStep& w, const uint8_t* rec, __amdgpu_buffer_rsrc_t a16,
                                            const int (&coff)[NCP], bool has_unit, int wave, int lane) {
@@ -754,7 +765,7 @@ __device__ __forceinline__ void tiled_step(f32x4 (&acc)[kUnitFrags][FM], int s, 
     tiled_copy_step<NCP>(a16, coff, nxt, sn, wave);
   }
   __builtin_amdgcn_sched_barrier(0);
-  load_unit_step(w, rec + static_cast<int64_t>(min(s + 2, S - 1)) * kRecBytes, lane);
+  load_unit_step<NT>(w, rec + static_cast<int64_t>(min(s + 2, S - 1)) * kRecBytes, lane);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -857,6 +868,7 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared<TR>& 
                                            UnitStep (&wb)[2], float my_g, int my_slot, float wg) {
   static_assert(16 * FMV <= TR, "the tile's groups fit the block's buffers");
   static_assert(MODE == 0 || TR == kTiledRows, "GEMM2's epilogue stages through the 128-row buffers");
+  constexpr bool kNT = TR == kTiledSmallRows;  // 16-row tiles: one tile per expert, records read once
   constexpr int NCP = FMV * 16 * 16 / kWave / kTiledWaves;  // copy instructions per wave and step
   const int row0 = b.row0, nrows = b.nrows, K = b.K, S = b.S, j = b.j;
   const bool has_unit = b.has_unit;
@@ -911,10 +923,10 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared<TR>& 
   // so that every wait above counts the same loads on every path
   int s = 0;
   for (; s + 1 < S; s += 2) {
-    tiled_step<FMV, NCP, A16>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
-    tiled_step<FMV, NCP, A16>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP, A16, kNT>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+    tiled_step<FMV, NCP, A16, kNT>(acc, s + 1, S, lds1, lds0, wb[1], rec, a16, coff, has_unit, wave, lane);
   }
-  if (s < S) tiled_step<FMV, NCP, A16>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
+  if (s < S) tiled_step<FMV, NCP, A16, kNT>(acc, s, S, lds0, lds1, wb[0], rec, a16, coff, has_unit, wave, lane);
 
   float ginv[FMV];
   int slots[FMV];
@@ -979,8 +991,9 @@ void moe_tiled_kernel(FwdParams p) {
   // nothing more.  The rows' global scales and slots are loaded here and
   // published by tiled_tile.
   UnitStep wb[2];
-  load_unit_step(wb[0], b.rec, lane);
-  load_unit_step(wb[1], b.rec + static_cast<int64_t>(min(1, b.S - 1)) * kRecBytes, lane);
+  constexpr bool kNT = TR == kTiledSmallRows;  // (as in tiled_tile)
+  load_unit_step<kNT>(wb[0], b.rec, lane);
+  load_unit_step<kNT>(wb[1], b.rec + static_cast<int64_t>(min(1, b.S - 1)) * kRecBytes, lane);
   float my_g = 1.0f;
   int my_slot = -1;
   // (W4A16: the activations carry no global scale)
