@@ -1168,8 +1168,18 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
       lds_set = true;
     }
   } else {
+    // GEMM1's grid takes the tightest bound on the batch's tiles: at most
+    // n = min(E, R) experts have rows, and an expert with c rows has
+    // ceil(c / mt) <= 1 + (c - 1) / mt tiles, so at most n + (R - n) / mt
+    // (plus the shared expert's).  Blocks past the last tile exit at once but
+    // still take a slot when dispatched: at one token on the large layer the
+    // looser bound (9 tile columns for 8 tiles) left 8 GEMM1 blocks per XCD
+    // waiting for the first ones to end.
+    const int64_t nact = std::min<int64_t>(p.E, p.R);
+    const int64_t tight = nact + (p.R - nact) / p.mt + (p.shared ? (p.T + p.mt - 1) / p.mt : 0);
+    const int gx1 = static_cast<int>(std::min<int64_t>(tight, max_tiles));
     const int nb1 = (p.I / 32) / (4 / KS1);
-    moe_stream_kernel<FM, KS1, 0, false><<<dim3(max_tiles, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
+    moe_stream_kernel<FM, KS1, 0, false><<<dim3(gx1, nb1), 256, stream_lds_total(FM, KS1, p.H), s>>>(p);
   }
   if (ev) (void)hipEventRecord(ev[2], s);
   const int nb2 = (p.H / 64) / (4 / KS2);
