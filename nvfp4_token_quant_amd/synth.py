@@ -62,6 +62,15 @@ LAYERS = {
     3: Layer(3, "prefill", 4096, 2048, 128, 8, 768, 0.02, 4096),
     4: Layer(4, "quantize", 16384, 7168),
     5: Layer(5, "large", 2048, 7168, 256, 8, 2048, 0.01, 8192),
+    # Shapes at the edges of what the library accepts (tests only): one
+    # expert and one K step in both GEMMs; more experts than the one-launch
+    # prologues take, the largest top-k, an odd number of K steps and a
+    # GEMM2 unit count not divisible by four; the tiled GEMMs with partial
+    # column bands; the largest expert count.
+    6: Layer(6, "edge-single", 9, 128, 1, 1, 128, 0.02, 16),
+    7: Layer(7, "edge-wide", 33, 384, 300, 16, 384, 0.02, 64),
+    8: Layer(8, "edge-tiled", 700, 640, 6, 3, 256, 0.02, 1024),
+    9: Layer(9, "edge-experts", 3, 256, 1024, 16, 128, 0.02, 8),
 }
 
 
