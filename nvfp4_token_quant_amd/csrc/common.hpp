@@ -156,16 +156,47 @@ __device__ __forceinline__ half2v e4m3_half2(uint32_t b) {
   return r;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Cross-lane exchanges of a wave in the vector ALU (no LDS round trip):
+// DPP within each row of 16 lanes, then v_permlane16_swap (rows 0 <-> 1,
+// 2 <-> 3) and v_permlane32_swap (lower <-> upper half).  DPP controls:
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <-> 7 - i of
+// each 8), row_mirror (lane i <-> 15 - i), row_ror 4 and 8.  Callers run
+// them with every lane of the wave active.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppRor4 = 0x124, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+// A value swapped with itself across a row pair (PAIR = 16) or the two
+// halves (PAIR = 32): each lane gets its own value in one result and its
+// partner's (lane ^ PAIR) in the other, so a commutative combination of the
+// two reduces over the pair whichever way round they come.
+template <int PAIR>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t& a, uint32_t& b) {
+  if constexpr (PAIR == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    static_assert(PAIR == 32, "row pairs or halves");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Maximum over the wave (exact, the same in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  uint32_t a, b;
+  lane_pair<16>(__float_as_uint(v), a, b);
+  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+  lane_pair<32>(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
 // Quantize one 16-element block held as binary32 values with global scale g,

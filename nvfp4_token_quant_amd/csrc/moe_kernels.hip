@@ -48,15 +48,14 @@ __device__ __forceinline__ int key_expert(uint64_t k) { return static_cast<int>(
 
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k >> 32), CTRL, 0xF, 0xF, false);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(k >> 32));
+  const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(k));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
 }
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
 
 __device__ __forceinline__ uint64_t row16_max(uint64_t k) {
   uint64_t o = dpp_u64<kDppXor1>(k); k = o > k ? o : k;
@@ -65,6 +64,8 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t k) {
   o = dpp_u64<kDppRor8>(k); k = o > k ? o : k;
   return k;
 }
+// (the association, and so the rounding, depends on the lane: a slot's weight
+// is normalized by the sum its own lane forms)
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<kDppXor1>(v);
   v += dpp_f32<kDppXor2>(v);
@@ -75,11 +76,17 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   k = row16_max(k);
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), o, kWave);
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), o, kWave);
-    const uint64_t ok = (static_cast<uint64_t>(hi) << 32) | lo;
-    k = ok > k ? ok : k;
+  for (int h = 0; h < 2; ++h) {
+    uint32_t ha, hb, la, lb;
+    if (h == 0) {
+      lane_pair<16>(static_cast<uint32_t>(k >> 32), ha, hb);
+      lane_pair<16>(static_cast<uint32_t>(k), la, lb);
+    } else {
+      lane_pair<32>(static_cast<uint32_t>(k >> 32), ha, hb);
+      lane_pair<32>(static_cast<uint32_t>(k), la, lb);
+    }
+    const uint64_t a = (static_cast<uint64_t>(ha) << 32) | la, b = (static_cast<uint64_t>(hb) << 32) | lb;
+    k = a > b ? a : b;
   }
   return k;
 }
@@ -88,44 +95,73 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
 // Router: the k largest logits of one token, ties to the smaller expert
 // index, slots in descending order; weights = exp(l_j - l_0) normalized over
 // the k slots (the softmax over all experts restricted to the chosen k).
-// One wave per token; lane l holds experts l, l+64, ...
+// Keys order the logits as binary32 compares do (-0 as +0) and, on equal
+// values, put the smaller expert first.
+//
+// Both routers below first sort each lane's keys (largest first) with
+// Batcher's odd-even merge sorting network (K. E. Batcher, "Sorting networks
+// and their applications", AFIPS 1968), so that each of the k selection
+// rounds only takes the maximum of the lanes' heads and pops the winning
+// lane's list.  Keys are unique (the expert index is part of them).  Slot j
+// ends in lane j of the token's lanes, and its weight is normalized by the
+// row-16 sum over the first 16 of them, so both routers give the same ids
+// and the same weights.
 // ---------------------------------------------------------------------------
-template <int kPerLane>
-__device__ void route_token_wave(const float* __restrict__ lrow, int E, int k,
-                                 int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                                 int32_t* __restrict__ lds_ids, int lane) {
-  // Unconditional loads (index clamped; invalid candidates get key 0) so
-  // that all of them are in flight at once.
-  float v[kPerLane];
+__device__ __forceinline__ void key_cx(uint64_t& a, uint64_t& b) {
+  const bool sw = b > a;
+  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+
+template <int N>
+__device__ __forceinline__ void sort_keys_desc(uint64_t (&c)[N]) {
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) v[i] = lrow[min(lane + kWave * i, E - 1)];
+  for (int p = 1; p < N; p <<= 1)
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) keep_issued(v[i]);
-  uint64_t cand[kPerLane];
+    for (int d = p; d >= 1; d >>= 1)
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+      for (int j = d % p; j + d < N; j += 2 * d)
+#pragma unroll
+        for (int i = 0; i < d; ++i)
+          if (i + j + d < N && (i + j) / (2 * p) == (i + j + d) / (2 * p)) key_cx(c[i + j], c[i + j + d]);
+}
+
+// One wave per token (few tokens: the shortest dependency chain); lane l
+// holds experts l, l + 64, ...; lane j < k returns slot j.
+template <int KPW>
+__device__ void route_token_wave(const float* __restrict__ lrow, int E, int k, int lane, int& my_id,
+                                 float& my_w) {
+  // unconditional loads (index clamped; invalid candidates get key 0), all
+  // in flight at once
+  float v[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) v[i] = lrow[min(lane + kWave * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) keep_issued(v[i]);
+  uint64_t cand[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
     const int e = lane + kWave * i;
     cand[i] = e < E ? route_key(v[i], e) : 0ull;
   }
+  sort_keys_desc<KPW>(cand);
   uint64_t mine = 0, top = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) best = cand[i] > best ? cand[i] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
-    if (lane == j) mine = best;
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    const uint64_t best = wave_max_u64(cand[0]);
     if (j == 0) top = best;
+    mine = lane == j ? best : mine;
+    const bool pop = cand[0] == best;
+#pragma unroll
+    for (int i = 0; i + 1 < KPW; ++i) cand[i] = pop ? cand[i + 1] : cand[i];
+    cand[KPW - 1] = pop ? 0ull : cand[KPW - 1];
   }
   const float ex = lane < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    const int id = key_expert(mine);
-    ids_out[lane] = id;
-    w_out[lane] = ex / sum;
-    lds_ids[lane] = id;
-  }
+  const float sum = row16_sum(ex);
+  my_id = key_expert(mine);
+  my_w = ex / sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -159,8 +195,14 @@ __global__ __launch_bounds__(256) void moe_route_kernel(FwdParams p, int tpb) {
       quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
                             p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
     }
-    route_token_wave<KPL>(p.logits + t * p.E, p.E, k, p.topk_ids + t * k, p.topk_w + t * k,
-                          s_ids + lt * k, lane);
+    int id;
+    float w;
+    route_token_wave<KPL>(p.logits + t * p.E, p.E, k, lane, id, w);
+    if (lane < k) {
+      p.topk_ids[t * k + lane] = id;
+      p.topk_w[t * k + lane] = w;
+      s_ids[lt * k + lane] = id;
+    }
     if (!p.deterministic) {
       float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
       for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -332,35 +374,9 @@ constexpr int kSmallMaxT = 256, kSmallMaxE = 256, kSmallMaxR = 2048;
 constexpr int kSmallThreads = 1024;  // 16 waves: 64 tokens routed per pass
 constexpr int kSmallWaves = kSmallThreads / 64;
 
-// Router for one token by a 16-lane group (lane gl of the group holds
-// experts gl, gl + 16, ...): lane j < k of the group ends with the j-th
-// chosen expert and its weight.  Each lane first sorts its KPL keys (largest
-// first) with Batcher's odd-even merge sorting network (K. E. Batcher,
-// "Sorting networks and their applications", AFIPS 1968), so that each of
-// the k selection rounds only takes the row maximum of the lanes' heads and
-// pops the winning lane's list, instead of rescanning all KPL keys of every
-// lane per round.  Keys are unique (the expert index is part of them), so the
-// selection is the same either way.
-__device__ __forceinline__ void key_cx(uint64_t& a, uint64_t& b) {
-  const bool sw = b > a;
-  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
-  a = hi;
-  b = lo;
-}
-
-template <int N>
-__device__ __forceinline__ void sort_keys_desc(uint64_t (&c)[N]) {
-#pragma unroll
-  for (int p = 1; p < N; p <<= 1)
-#pragma unroll
-    for (int d = p; d >= 1; d >>= 1)
-#pragma unroll
-      for (int j = d % p; j + d < N; j += 2 * d)
-#pragma unroll
-        for (int i = 0; i < d; ++i)
-          if (i + j + d < N && (i + j) / (2 * p) == (i + j + d) / (2 * p)) key_cx(c[i + j], c[i + j + d]);
-}
-
+// Router for one token by a 16-lane group (4 tokens per wave; lane gl of
+// the group holds experts gl, gl + 16, ...): lane j < k of the group ends
+// with slot j (the sorted-list selection of the router section above).
 template <int KPL>
 __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k, int gl,
                                     int& my_id, float& my_w) {
@@ -510,7 +526,8 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
 
 // ---------------------------------------------------------------------------
 // Prologue for decode-sized batches (T <= 64, E <= 256): block 0 routes every
-// token (16 lanes per token, all tokens in one pass) and keeps, per expert,
+// token (a whole wave per token up to kTinyWaveRouteT tokens, else 16 lanes
+// per token, all tokens in one pass) and keeps, per expert,
 // the 64-bit mask of the tokens routed to it.  A row's place in the stable
 // expandInputRows order is then the expert's offset plus the popcount of the
 // mask below its token, and the counts come from the masks as well, so the
@@ -519,6 +536,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
 // t + 256, ...; the row amax is one LDS exchange between four waves).
 // ---------------------------------------------------------------------------
 constexpr int kTinyMaxT = 64, kTinyMaxE = 256;
+constexpr int kTinyWaveRouteT = 8;  // tokens routed one per wave (see step 1)
 
 template <int NBL, int KPL>
 __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdParams p) {
@@ -588,9 +606,23 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
   __shared__ int32_t s_wsum[2][4];
   if (tid < kTinyMaxE) s_mask[tid] = 0ull;
   __syncthreads();
-  // 1. top-k of every token: wave w, group g routes token 4 w + g (waves
-  // past the last token skip it)
-  if (4 * wave < T) {
+  // 1. top-k of every token.  Up to kTinyWaveRouteT tokens: wave w routes
+  // token w with all its lanes (the shortest chain: the block's routing is
+  // the prologue's critical path); more: wave w, group g routes token
+  // 4 w + g.  Waves past the last token skip it.
+  if (T <= kTinyWaveRouteT) {
+    if (wave < T) {
+      int id;
+      float w;
+      route_token_wave<(KPL >= 4 ? KPL / 4 : 1)>(p.logits + static_cast<int64_t>(wave) * E, E, k, lane, id, w);
+      if (lane < k) {
+        p.topk_ids[wave * k + lane] = id;
+        p.topk_w[wave * k + lane] = w;
+        s_ids[wave * k + lane] = id;
+        atomicOr(reinterpret_cast<unsigned long long*>(&s_mask[id]), 1ull << wave);
+      }
+    }
+  } else if (4 * wave < T) {
     const int grp = lane >> 4, gl = lane & 15;
     const int tk = 4 * wave + grp;
     int id;
