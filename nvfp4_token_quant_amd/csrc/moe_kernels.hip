@@ -91,6 +91,49 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return k;
 }
 
+// Inclusive prefix sum over the wave's lanes (every lane active): steps of
+// 1, 2, 4, 8 lanes within each 16-lane row (DPP row_shr; a lane shifted in
+// from outside the row adds 0), then every row adds the totals of the rows
+// below it (lanes 15, 31, 47).
+__device__ __forceinline__ int wave_scan_incl(int v, int lane) {
+  v += static_cast<int>(dpp_u32<0x111>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_u32<0x112>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_u32<0x114>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_u32<0x118>(static_cast<uint32_t>(v)));
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// Inclusive prefix sums of two values over threads 0..255 of a block (its
+// first four waves): a wave scan each, then every wave adds the totals of
+// the waves below it, exchanged through s_tot (one barrier).  Every thread
+// of the block calls it; threads past 255 keep their values.  Returns the
+// two totals over the 256 threads.
+__device__ __forceinline__ int2 scan256_pair(int& a, int& b, int tid, int (&s_tot)[2][4]) {
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  if (wave < 4) {
+    a = wave_scan_incl(a, lane);
+    b = wave_scan_incl(b, lane);
+    if (lane == kWave - 1) {
+      s_tot[0][wave] = a;
+      s_tot[1][wave] = b;
+    }
+  }
+  __syncthreads();
+  int2 tot = make_int2(0, 0);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave && wave < 4) {
+      a += s_tot[0][w];
+      b += s_tot[1][w];
+    }
+    tot.x += s_tot[0][w];
+    tot.y += s_tot[1][w];
+  }
+  return tot;
+}
+
 // ---------------------------------------------------------------------------
 // Router: the k largest logits of one token, ties to the smaller expert
 // index, slots in descending order; weights = exp(l_j - l_0) normalized over
@@ -255,12 +298,7 @@ __global__ __launch_bounds__(kSchedThreads) void moe_schedule_kernel(FwdParams p
     }
   }
   // inclusive scan over the expert's chunks
-  int inc = sum;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int a = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += a;
-  }
+  int inc = wave_scan_incl(sum, lane);
   const bool second = c >= kWave;
   if (!second && lane == kWave - 1) s_wave[le] = inc;
   __syncthreads();
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(kSchedThreads) void moe_schedule_kernel(FwdParams p
 __global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
   __shared__ int32_t s_off[kMaxExperts];
   __shared__ int32_t s_tb[kMaxExperts];
-  __shared__ int32_t s_part[256][2];
+  __shared__ int s_tot[2][4];
   const int tid = threadIdx.x;
   const int E = p.E, mt = p.mt;
   const int per = (E + 255) / 256;
@@ -310,21 +348,10 @@ __global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
       tsum += (cnt + mt - 1) / mt;
     }
   }
-  s_part[tid][0] = rsum;
-  s_part[tid][1] = tsum;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int a0 = 0, a1 = 0;
-    if (tid >= o) {
-      a0 = s_part[tid - o][0];
-      a1 = s_part[tid - o][1];
-    }
-    __syncthreads();
-    s_part[tid][0] += a0;
-    s_part[tid][1] += a1;
-    __syncthreads();
-  }
-  int rb = s_part[tid][0] - rsum, tb = s_part[tid][1] - tsum;
+  int rb = rsum, tb = tsum;
+  const int2 total = scan256_pair(rb, tb, tid, s_tot);
+  rb -= rsum;
+  tb -= tsum;
   for (int u = 0; u < per; ++u) {
     const int e = tid * per + u;
     if (e < E) {
@@ -344,8 +371,8 @@ __global__ __launch_bounds__(256) void moe_place_kernel(FwdParams p, int tpb) {
       for (int i = 0; i < nt; ++i) p.tiles[s_tb[e] + i] = make_int4(e, s_off[e] + i * mt, min(mt, cnt - i * mt), 0);
     }
     if (tid == 255) {
-      p.offsets[E] = s_part[255][0];
-      *p.n_tiles = append_shared_tiles(p, s_part[255][1]);
+      p.offsets[E] = total.x;
+      *p.n_tiles = append_shared_tiles(p, total.y);
     }
   }
   const int i = blockIdx.x * 256 + tid;
@@ -438,7 +465,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   __shared__ int32_t s_cnt[kSmallMaxR / 64][kSmallMaxE];
   __shared__ int32_t s_off[kSmallMaxE];
   __shared__ int32_t s_tbase[kSmallMaxE];
-  __shared__ int32_t s_part[kSmallThreads][2];
+  __shared__ int s_tot[2][4];
   const int tid = threadIdx.x;
   // 1. routing, 4 tokens per wave at a time
   const int grp = lane >> 4, gl = lane & 15;
@@ -487,23 +514,12 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
     ntile = (tot + p.mt - 1) / p.mt;
     p.counts[tid] = tot;
   }
-  s_part[tid][0] = tot;
-  s_part[tid][1] = ntile;
-  __syncthreads();
   // 4. exclusive scans over experts (rows and tiles)
-  for (int o = 1; o < kSmallMaxE; o <<= 1) {
-    int a0 = 0, a1 = 0;
-    if (tid >= o) {
-      a0 = s_part[tid - o][0];
-      a1 = s_part[tid - o][1];
-    }
-    __syncthreads();
-    s_part[tid][0] += a0;
-    s_part[tid][1] += a1;
-    __syncthreads();
-  }
+  static_assert(kSmallMaxE == 256, "one scan over the first four waves");
+  int incr = tot, inct = ntile;
+  const int2 total = scan256_pair(incr, inct, tid, s_tot);
   if (tid < E) {
-    const int off = s_part[tid][0] - tot, tb = s_part[tid][1] - ntile;
+    const int off = incr - tot, tb = inct - ntile;
     s_off[tid] = off;
     s_tbase[tid] = tb;
     p.offsets[tid] = off;
@@ -511,8 +527,8 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
       p.tiles[tb + i] = make_int4(tid, off + i * p.mt, min(p.mt, tot - i * p.mt), 0);
   }
   if (tid == kSmallMaxE - 1) {
-    p.offsets[E] = s_part[kSmallMaxE - 1][0];
-    *p.n_tiles = append_shared_tiles(p, s_part[kSmallMaxE - 1][1]);
+    p.offsets[E] = total.x;
+    *p.n_tiles = append_shared_tiles(p, total.y);
   }
   __syncthreads();
   // 5. placement
@@ -641,16 +657,8 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
   if (tid < kTinyMaxE) {
     cnt = tid < E ? __popcll(s_mask[tid]) : 0;
     nt = (cnt + p.mt - 1) / p.mt;
-    ic = cnt;
-    it = nt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int a = __shfl_up(ic, o, kWave), b = __shfl_up(it, o, kWave);
-      if (lane >= o) {
-        ic += a;
-        it += b;
-      }
-    }
+    ic = wave_scan_incl(cnt, lane);
+    it = wave_scan_incl(nt, lane);
     if (lane == kWave - 1) {
       s_wsum[0][wave] = ic;
       s_wsum[1][wave] = it;
