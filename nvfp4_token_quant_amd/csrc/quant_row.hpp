@@ -100,7 +100,7 @@ __device__ __forceinline__ void quantize_row_regs(const RowRegs<NB>& rr, int nbl
 }
 
 template <int NB>
-__device__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
+__device__ __forceinline__ void quantize_row_wave(const uint16_t* __restrict__ xrow, int nblk,
                                   uint8_t* __restrict__ crow, uint8_t* __restrict__ srow,
                                   float* __restrict__ gout, int lane, _Float16* __restrict__ x16row = nullptr,
                                   const float* gfix = nullptr) {

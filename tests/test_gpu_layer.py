@@ -143,14 +143,15 @@ def test_layer3_prefill_full():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("T", [1, 7, 2048, 8192])
+@pytest.mark.parametrize("T", [1, 7, 2048, 8192, 200])
 def test_layer5_large(T):
     """Large layer (H = 7168, E = 256, I = 2048, Zipf(1.2) routing with 8
     experts never chosen), workspace ceiling 8192 (the largest forward it
     accepts).  Every integer output and the re-quantization of every
     expanded row; the layer output and the SwiGLU output on every token for
     T <= 7, and above on the tokens that cover every active expert's first
-    and last expanded row (every tile shape the kernels run)."""
+    and last expanded row (every tile shape the kernels run).  T = 200 takes
+    the small-batch prologue with this layer's row length."""
     L = synth.LAYERS[5]
     print(f"layer 5 T={T} (ceiling {L.max_tokens})", flush=True)
     x, logits = synth.activations(5, T), synth.router_logits(5, T)
