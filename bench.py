@@ -17,7 +17,9 @@ Timing: `steps` forwards after `warmup` untimed ones, bracketed by
 synchronizations; wall time gives `value` (tokens/s).  By default the timed
 forwards are captured into one HIP graph and replayed once (a decode
 deployment replays one graph per model step holding every layer; `--eager`
-launches the kernels directly).  Every timed forward
+launches the kernels directly); after the graph replay the same forwards are
+also timed launched directly, without stage events (`eager_ms_per_step`,
+reported beside `ms_per_step`).  Every timed forward
 records HIP events around its four kernels on its own stream, which give
 each kernel's mean duration; the dominant kernel's algorithmic bytes (or
 FLOPs) over that duration is `roofline.achieved`.  Expert weights rotate over
@@ -156,8 +158,8 @@ def main():
         for lid, T in CONFIGS:
             e = bench_quantize(args, T, args.config_cpu_budget_s) if lid == 4 else \
                 bench_layer(args, lid, T, args.config_cpu_budget_s)
-            configs.append({key: e[key] for key in ("config", "value", "unit", "ms_per_step", "roofline",
-                                                   "layer_roofline", "cpu_baseline") if key in e})
+            configs.append({key: e[key] for key in ("config", "value", "unit", "ms_per_step", "eager_ms_per_step",
+                                                   "roofline", "layer_roofline", "cpu_baseline") if key in e})
             print(f"bench: {e['config']['workload']} T={e['config']['T']}: {e['ms_per_step']:.4f} ms/step, "
                   f"{e['roofline']['bound']} frac {e['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
         res["configs"] = configs
@@ -311,6 +313,18 @@ def bench_layer(args, layer_id, T, cpu_budget_s):
             hip.destroy(e)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = T * args.steps / (t1 - t0)
+    eager_ms = None
+    if not args.eager:
+        # the same forwards launched directly (no graph, no stage events), for
+        # reference next to the graph replay above
+        for ly in layers:
+            lib.moe_workspace_set_stage_events(ly.handle, None)
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        for i in range(args.steps):
+            fwd(layers[i % len(layers)])
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - e0) * 1e3 / args.steps
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
     workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "") + \
@@ -347,6 +361,7 @@ def bench_layer(args, layer_id, T, cpu_budget_s):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "eager_ms_per_step": eager_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
