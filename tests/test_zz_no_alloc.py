@@ -30,6 +30,8 @@ def _inputs(layer_id, T):
     (2, (300, 200), True, None),     # three-kernel and small-batch prologues
     (1, (256, 16), True, "average"),  # tiled GEMMs, then stream GEMMs; shared expert
     (2, (64, 7), False, None),       # atomic finalize
+    (7, (33, 5), True, "sum"),       # 300 experts, top-16: three-kernel and one-block prologues
+    (5, (7, 1), True, None),         # the large layer at a few tokens (7168-wide rows)
 ])
 def test_noalloc_matches_workspace_forward(layer_id, Ts, deterministic, shared):
     L = synth.LAYERS[layer_id]
