@@ -1,8 +1,9 @@
-"""Captured forwards of the prefill path (tiled GEMMs, the separate
-re-quantization / bf16 conversion kernel) replay bit-identically to eager
-forwards, for the NVFP4 layer, the W4A16 layer and the layer with a shared
-expert; every replay is checked, with eager work and synchronizations between
-the replays."""
+"""Captured forwards replay like eager forwards: the prefill path (tiled
+GEMMs, the separate re-quantization / bf16 conversion kernel) for the NVFP4
+layer, the W4A16 layer and the layer with a shared expert, the forward on
+handed-over codes, and the decode-sized path (one-block prologue, stream
+GEMMs) in both finalize modes; every replay is checked, with eager work and
+synchronizations between the replays."""
 import numpy as np
 import pytest
 import torch
@@ -79,5 +80,47 @@ def test_prequantized_forward_graph_replay(T):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
         layer.forward_into(x[:17], logits[:17], other, T=17)   # eager work between replays
+        torch.cuda.synchronize()
+    layer.close()
+
+
+@pytest.mark.parametrize("T,deterministic", [(1, True), (7, True), (64, True), (7, False)])
+def test_stream_forward_graph_replay(T, deterministic):
+    """Decode-sized forwards (one-block prologue with either router, stream
+    GEMMs) captured and replayed: every replay equals the eager forward, bit
+    for bit in the slot-ordered finalize, within a few bf16 ulps with the
+    atomic one (fp32 adds in arrival order)."""
+    L = synth.LAYERS[2]
+    print(f"graph replay, layer 2 T={T} deterministic={deterministic}", flush=True)
+    layer = binding.MoeLayer(64, L.H, L.I, L.E, L.k, deterministic)
+    layer.bind(gpu_weights(2))
+    x = to_device_bf16(synth.activations(2, T))
+    logits = torch.from_numpy(synth.router_logits(2, T)).cuda()
+    out = torch.empty_like(x)
+    layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    eager = out.float().cpu().numpy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward_into(x, logits, out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward_into(x, logits, out)
+    torch.cuda.synchronize()
+    other = torch.empty((64, L.H), dtype=torch.bfloat16, device="cuda")
+    xo = to_device_bf16(synth.activations(2, 64))
+    lo = torch.from_numpy(synth.router_logits(2, 64)).cuda()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        if deterministic:
+            np.testing.assert_array_equal(got, eager)
+        else:
+            assert np.abs(got - eager).max() <= 4 * 2.0 ** -8 * np.abs(eager).max()
+        layer.forward_into(xo, lo, other)   # eager work on another batch between replays
         torch.cuda.synchronize()
     layer.close()
