@@ -12,7 +12,8 @@ Batch sizes cover the decode-sized, small-batch and three-kernel prologues and
 both re-quantization paths (fused into the GEMM2 stream kernel, and the
 separate kernel before the tiled GEMM2), up to the prefill-shaped layer at full
 size (T = 4096; its layer output on the tokens covering every expert's first
-and last expanded row)."""
+and last expanded row), and the large layer at one and seven tokens (rows of
+7168, GEMM2's K of 2048)."""
 import numpy as np
 import pytest
 import torch
@@ -48,7 +49,7 @@ def _scales(layer_id, x, ids, w, T):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 256), (2, 64), (2, 301), (3, 4096)])
+@pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 256), (2, 64), (2, 301), (3, 4096), (5, 1), (5, 7)])
 def test_static_scales_parity(layer_id, T):
     L = synth.LAYERS[layer_id]
     print(f"layer {layer_id} T={T} static scales", flush=True)
