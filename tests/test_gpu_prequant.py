@@ -38,7 +38,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("layer_id,T", [(1, 16), (2, 64), (2, 301), (3, 4096)])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("layer_id,T", [(1, 16), (2, 64), (2, 301), (3, 4096), (5, 1), (5, 7)])
 def test_prequantized_forward_equals_forward(layer_id, T):
     L = synth.LAYERS[layer_id]
     print(f"layer {layer_id} T={T} pre-quantized vs forward", flush=True)

@@ -85,6 +85,14 @@ def test_shared_decode_stream_path(strategy, deterministic):
     _check(2, 64, strategy, deterministic)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 7])
+def test_shared_large_layer(T):
+    """The large layer (rows of 7168, 257 expert weight sets) with its shared
+    expert at one and seven tokens."""
+    _check(5, T, "sum")
+
+
 @pytest.mark.parametrize("T,deterministic", [(160, True), (256, False)])
 def test_shared_tiled_path(T, deterministic):
     """The tiny layer at batch sizes that take the tiled GEMMs."""
