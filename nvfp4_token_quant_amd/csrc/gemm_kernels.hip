@@ -21,6 +21,7 @@
 // use its 8-code pieces q = 0..3, and the token operand uses the same k
 // assignment (lane group g holds k = 32g + 8q + i), so every k is summed once.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -1158,14 +1159,19 @@ static void launch_stream(const FwdParams& p, int max_tiles, hipStream_t s, hipE
     static_assert(FM * 16 <= kTiledSmallRows, "the stream path's tiles fit the small tiled blocks");
     const int nbt = (p.I / 32 + kTiledWaves - 1) / kTiledWaves;
     moe_tiled_kernel<0, true, kTiledSmallRows><<<p.tiled_gx * nbt, kTiledThreads, 0, s>>>(p);
-    // GEMM2's bf16 staging may take more than the default 64 KB of dynamic LDS
-    static bool lds_set = false;
-    if (!lds_set) {
+    // GEMM2's bf16 staging may take more than the default 64 KB of dynamic
+    // LDS.  The attribute belongs to the current device: set once per device
+    // (devices past the mask's 64 set it on every call).
+    static std::atomic<uint64_t> lds_set{0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+    if (bit == 0 || (lds_set.load(std::memory_order_relaxed) & bit) == 0) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_stream_kernel<FM, KS2, 1, A16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kStreamA16MaxLds);
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_stream_kernel<FM, KS2, 1, A16, true>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kStreamA16MaxLds);
-      lds_set = true;
+      lds_set.fetch_or(bit, std::memory_order_relaxed);
     }
   } else {
     // GEMM1's grid takes the tightest bound on the batch's tiles: at most
