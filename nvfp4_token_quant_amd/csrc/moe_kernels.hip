@@ -33,7 +33,7 @@ namespace nvfp4 {
 // equal logits, the smaller expert index.  -0.0 is keyed as +0.0: a binary32
 // comparison finds the two equal, so their tie also goes to the smaller
 // index.  Reductions over a 16-lane DPP row use quad permutes (xor 1, xor 2)
-// and row rotates (4, 8), a few cycles each.
+// and row rotates (4, 8), one instruction each.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
   const uint32_t u = __float_as_uint(v) == 0x80000000u ? 0u : __float_as_uint(v);
@@ -47,22 +47,37 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 __device__ __forceinline__ int key_expert(uint64_t k) { return static_cast<int>(~static_cast<uint32_t>(k)); }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
-  const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(k >> 32));
-  const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(k));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
 }
 
-__device__ __forceinline__ uint64_t row16_max(uint64_t k) {
-  uint64_t o = dpp_u64<kDppXor1>(k); k = o > k ? o : k;
-  o = dpp_u64<kDppXor2>(k); k = o > k ? o : k;
-  o = dpp_u64<kDppRor4>(k); k = o > k ? o : k;
-  o = dpp_u64<kDppRor8>(k); k = o > k ? o : k;
-  return k;
+// The largest key over a 16-lane DPP row, or over the wave, as two 32-bit
+// maxima: of the high words (the ordered logits), then of the low words
+// (~expert) of the lanes whose high word is that maximum.  The pair is the
+// lexicographic, i.e. 64-bit, maximum; each DPP step is a single max with a
+// DPP operand (the 64-bit form takes two moves, a compare and two selects).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppRor4>(v));
+  v = max(v, dpp_u32<kDppRor8>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max_u32(v);
+  uint32_t a, b;
+  lane_pair<16>(v, a, b);
+  v = max(a, b);
+  lane_pair<32>(v, a, b);
+  return max(a, b);
+}
+template <bool WAVE>
+__device__ __forceinline__ uint64_t key_max(uint64_t k) {
+  const uint32_t h = static_cast<uint32_t>(k >> 32), l = static_cast<uint32_t>(k);
+  const uint32_t mh = WAVE ? wave_max_u32(h) : row16_max_u32(h);
+  const uint32_t tl = h == mh ? l : 0u;
+  const uint32_t ml = WAVE ? wave_max_u32(tl) : row16_max_u32(tl);
+  return (static_cast<uint64_t>(mh) << 32) | ml;
 }
 // (the association, and so the rounding, depends on the lane: a slot's weight
 // is normalized by the sum its own lane forms)
@@ -72,23 +87,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<kDppRor4>(v);
   v += dpp_f32<kDppRor8>(v);
   return v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  k = row16_max(k);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t ha, hb, la, lb;
-    if (h == 0) {
-      lane_pair<16>(static_cast<uint32_t>(k >> 32), ha, hb);
-      lane_pair<16>(static_cast<uint32_t>(k), la, lb);
-    } else {
-      lane_pair<32>(static_cast<uint32_t>(k >> 32), ha, hb);
-      lane_pair<32>(static_cast<uint32_t>(k), la, lb);
-    }
-    const uint64_t a = (static_cast<uint64_t>(ha) << 32) | la, b = (static_cast<uint64_t>(hb) << 32) | lb;
-    k = a > b ? a : b;
-  }
-  return k;
 }
 
 // Inclusive prefix sum over the wave's lanes (every lane active): steps of
@@ -193,7 +191,7 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k, i
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j >= k) break;
-    const uint64_t best = wave_max_u64(cand[0]);
+    const uint64_t best = key_max<true>(cand[0]);
     if (j == 0) top = best;
     mine = lane == j ? best : mine;
     const bool pop = cand[0] == best;
@@ -423,7 +421,7 @@ __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j >= k) break;
-    const uint64_t best = row16_max(cand[0]);
+    const uint64_t best = key_max<false>(cand[0]);
     if (j == 0) top = best;
     mine = gl == j ? best : mine;
     const bool pop = cand[0] == best;  // this lane held the winner
@@ -891,7 +889,8 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
     }
   }
   if (ev) (void)hipEventRecord(ev[1], s);
-  launch_grouped_gemms(p, max_tiles, s, ev);
+  const hipError_t ge = launch_grouped_gemms(p, max_tiles, s, ev);
+  if (ge != hipSuccess) return ge;
   const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 4);
   moe_finalize_kernel<<<static_cast<unsigned>((nthreads + 255) / 256), 256, 0, s>>>(p);
   if (ev) (void)hipEventRecord(ev[4], s);
