@@ -168,6 +168,28 @@ __device__ __forceinline__ void sort_keys_desc(uint64_t (&c)[N]) {
           if (i + j + d < N && (i + j) / (2 * p) == (i + j + d) / (2 * p)) key_cx(c[i + j], c[i + j + d]);
 }
 
+// The k selection rounds over the lanes' sorted lists (KMAX >= k rounds at
+// most): each round takes the largest head over the 16-lane row (or the
+// wave) and pops it from the lane that held it; lane j keeps round j's key.
+// After round j at most KMAX - 1 - j more pops follow, so only that many
+// leading entries of a list can still become its head and only those are
+// shifted.
+template <int N, int KMAX, bool WAVE>
+__device__ __forceinline__ void select_rounds(uint64_t (&cand)[N], int k, int lane, uint64_t& mine,
+                                              uint64_t& top) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const uint64_t best = key_max<WAVE>(cand[0]);
+      if (j == 0) top = best;
+      mine = lane == j ? best : mine;
+      const bool pop = cand[0] == best;  // this lane held the winner
+#pragma unroll
+      for (int i = 0; i < N && i + 1 < KMAX - j; ++i) cand[i] = pop ? (i + 1 < N ? cand[i + 1] : 0ull) : cand[i];
+    }
+  }
+}
+
 // One wave per token (few tokens: the shortest dependency chain); lane l
 // holds experts l, l + 64, ...; lane j < k returns slot j.
 template <int KPW>
@@ -188,17 +210,10 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k, i
   }
   sort_keys_desc<KPW>(cand);
   uint64_t mine = 0, top = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    const uint64_t best = key_max<true>(cand[0]);
-    if (j == 0) top = best;
-    mine = lane == j ? best : mine;
-    const bool pop = cand[0] == best;
-#pragma unroll
-    for (int i = 0; i + 1 < KPW; ++i) cand[i] = pop ? cand[i + 1] : cand[i];
-    cand[KPW - 1] = pop ? 0ull : cand[KPW - 1];
-  }
+  if (k <= 8)
+    select_rounds<KPW, 8, true>(cand, k, lane, mine, top);
+  else
+    select_rounds<KPW, kMaxTopK, true>(cand, k, lane, mine, top);
   const float ex = lane < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
   const float sum = row16_sum(ex);
   my_id = key_expert(mine);
@@ -418,17 +433,10 @@ __device__ void route_token_group16(const float* __restrict__ lrow, int E, int k
   }
   sort_keys_desc<KPL>(cand);
   uint64_t mine = 0, top = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    const uint64_t best = key_max<false>(cand[0]);
-    if (j == 0) top = best;
-    mine = gl == j ? best : mine;
-    const bool pop = cand[0] == best;  // this lane held the winner
-#pragma unroll
-    for (int i = 0; i + 1 < KPL; ++i) cand[i] = pop ? cand[i + 1] : cand[i];
-    cand[KPL - 1] = pop ? 0ull : cand[KPL - 1];
-  }
+  if (k <= 8)
+    select_rounds<KPL, 8, false>(cand, k, gl, mine, top);
+  else
+    select_rounds<KPL, kMaxTopK, false>(cand, k, gl, mine, top);
   const float ex = gl < k ? expf(key_value(mine) - key_value(top)) : 0.0f;
   const float sum = row16_sum(ex);
   my_id = key_expert(mine);
