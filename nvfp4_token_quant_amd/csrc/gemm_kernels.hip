@@ -137,11 +137,19 @@ __device__ __forceinline__ uint32_t requant_block(const float* __restrict__ src,
   return quantize_block16(f, g2, lo, hi);
 }
 
+// Four binary32 values -> four bf16 (nearest even), element 0 in the low half.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16),
+                    f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16));
+}
+
 // GEMM2: per lane, fragment f holds y[n = n0 + 16 f + 4g + i] of row m =
 // 16 fm + r16; ginv[fm] = 1 / (that row's a2 global scale), slot[fm] = its
 // t*k+j, wginv = 1 / (the expert's W2 global scale).  y is stored by slot
 // (row t*k+j of y is token t's j-th expert output), so the finalize reads
-// each token's k rows contiguously, without the inverse permutation.
+// each token's k rows contiguously, without the inverse permutation.  Like
+// the layer's input and output, the expanded rows' outputs are held in bf16
+// (rounded to nearest even); the finalize sums them in binary32.
 template <int FM, int FN>
 __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&acc)[FN][FM], int e,
                                             int row0, int nrows, int n0, const float (&ginv)[FM],
@@ -158,7 +166,7 @@ __device__ __forceinline__ void g2_epilogue(const FwdParams& p, const f32x4 (&ac
       const float y0 = acc[f][fm][0] * alpha, y1 = acc[f][fm][1] * alpha;
       const float y2 = acc[f][fm][2] * alpha, y3 = acc[f][fm][3] * alpha;
       if (p.deterministic) {
-        *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(slot[fm]) * H + n) = make_float4(y0, y1, y2, y3);
+        *reinterpret_cast<uint2*>(p.y + static_cast<int64_t>(slot[fm]) * H + n) = pack_bf16x4(y0, y1, y2, y3);
       } else {
         const float w = slot_weight(p, slot[fm]);
         float* dst = p.out_acc + static_cast<int64_t>(slot_token(p, slot[fm])) * H + n;
@@ -841,13 +849,18 @@ __device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared<
     }
     const int nr = min(32, nrows - 16 * r);
     if (p.deterministic) {
-      // lane l: row 4 i + l / 16, columns 4 (l % 16) .. + 3
-      for (int i = 0; 4 * i < nr; ++i) {
-        const int m = 4 * i + (lane >> 4);
+      // lane l: row 8 i + l / 8, columns 8 (l % 8) .. + 7 (one 16-byte bf16
+      // store; eight 128-byte row segments per instruction)
+      for (int i = 0; 8 * i < nr; ++i) {
+        const int m = 8 * i + (lane >> 3);
         if (m < nr) {
-          const float4 v = *reinterpret_cast<const float4*>(st + m * kAtomicPitch + 4 * (lane & 15));
+          const float* src = st + m * kAtomicPitch + 8 * (lane & 7);
+          const float4 a = *reinterpret_cast<const float4*>(src);
+          const float4 c = *reinterpret_cast<const float4*>(src + 4);
+          const uint2 lo = pack_bf16x4(a.x, a.y, a.z, a.w), hi = pack_bf16x4(c.x, c.y, c.z, c.w);
           // y by slot (see g2_epilogue)
-          *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(sh.slot[16 * r + m]) * H + n0 + 4 * (lane & 15)) = v;
+          *reinterpret_cast<uint4*>(p.y + static_cast<int64_t>(sh.slot[16 * r + m]) * H + n0 + 8 * (lane & 7)) =
+              make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
       }
     } else {

@@ -98,7 +98,7 @@ struct FwdParams {
   float* a2_g;
   _Float16* a2q16;  // [Rt, I] dequantized re-quantized act (exact in fp16); tiled path only
                     // (W4A16: act rounded to bf16, the same 16-bit slots)
-  float* y;        // [Rt, H] (deterministic finalize)
+  uint16_t* y;     // [Rt, H] bf16 expert outputs by slot (deterministic finalize)
   float* out_acc;  // [T, H] (atomic finalize)
   // weights: unit records (see kRecBytes) and per-expert global scales
   const uint8_t* w13;

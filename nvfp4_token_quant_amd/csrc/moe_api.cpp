@@ -138,7 +138,7 @@ int64_t layout_buffers(const moe_config& c, int64_t T_cap, bool own_gscales, uin
   take(&b->a2_scales, Rt * I / 16);
   take(&b->a2_g, Rt * 4);
   take(&b->a2q16, Rt * I * 2);
-  take(&b->y, det ? Rt * H * 4 : 0);
+  take(&b->y, det ? Rt * H * 2 : 0);
   take(&b->out_acc, det ? 0 : T * H * 4);
   take(&b->w13g, own_gscales ? Ew * 4 : 0);
   take(&b->w2g, own_gscales ? Ew * 4 : 0);

@@ -733,56 +733,66 @@ static void launch_prologue_small(const FwdParams& p, hipStream_t s) {
 }
 
 // Finalize: out[t, n] = bf16_rne(sum_j w[t, j] * y[t * k + j, n]) in slot
-// order (deterministic; GEMM2 stores y by slot), or bf16_rne(out_acc[t, n])
-// after the atomic epilogue.
+// order (deterministic; GEMM2 stores y by slot, in bf16), or
+// bf16_rne(out_acc[t, n]) after the atomic epilogue.
 // With a shared expert the deterministic sum adds its row R + t last and the
 // total is multiplied by the combination scale (1 or 0.5, exact); the atomic
 // epilogue applies the scale to each contribution.
-// One thread per 4 output columns; the slots are taken 8 at a time with all
-// their weight and y loads issued before the sums.
+// One thread per 8 output columns (16-byte loads of y, one 16-byte store);
+// the slots are taken 8 at a time with all their weight and y loads issued
+// before the sums.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
 __global__ __launch_bounds__(256) void moe_finalize_kernel(FwdParams p) {
   const int H = p.H, k = p.k;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int per_row = H / 4;
+  const int per_row = H / 8;
   if (idx >= static_cast<int64_t>(p.T) * per_row) return;
   const int64_t t = idx / per_row;
-  const int n = static_cast<int>(idx % per_row) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int n = static_cast<int>(idx % per_row) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (p.deterministic) {
     for (int j0 = 0; j0 < k; j0 += 8) {
       float w[8];
-      float4 y[8];
+      uint4 y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // GEMM2 stored y by slot: token t's rows are t*k .. t*k + k - 1
         const int64_t sl = t * k + min(j0 + j, k - 1);
         w[j] = j0 + j < k ? p.topk_w[sl] : 0.0f;
-        y[j] = *reinterpret_cast<const float4*>(p.y + sl * H + n);
+        y[j] = *reinterpret_cast<const uint4*>(p.y + sl * H + n);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j0 + j < k) {
-          acc.x += w[j] * y[j].x;
-          acc.y += w[j] * y[j].y;
-          acc.z += w[j] * y[j].z;
-          acc.w += w[j] * y[j].w;
+          float f[8];
+          bf16x8_to_f32(y[j], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += w[j] * f[i];
         }
       }
     }
     if (p.shared) {
-      const float4 ys = *reinterpret_cast<const float4*>(p.y + (p.R + t) * H + n);
-      acc.x = (acc.x + ys.x) * p.combine;
-      acc.y = (acc.y + ys.y) * p.combine;
-      acc.z = (acc.z + ys.z) * p.combine;
-      acc.w = (acc.w + ys.w) * p.combine;
+      float f[8];
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(p.y + (p.R + t) * H + n), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = (acc[i] + f[i]) * p.combine;
     }
   } else {
-    acc = *reinterpret_cast<const float4*>(p.out_acc + t * H + n);
+    const float4 a = *reinterpret_cast<const float4*>(p.out_acc + t * H + n);
+    const float4 b = *reinterpret_cast<const float4*>(p.out_acc + t * H + n + 4);
+    acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+    acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
   }
-  uint2 o;
-  o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
-  o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
-  *reinterpret_cast<uint2*>(p.out + t * H + n) = o;
+  uint4 o;
+  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(p.out + t * H + n) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -899,7 +909,7 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
   if (ev) (void)hipEventRecord(ev[1], s);
   const hipError_t ge = launch_grouped_gemms(p, max_tiles, s, ev);
   if (ge != hipSuccess) return ge;
-  const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 4);
+  const int64_t nthreads = static_cast<int64_t>(p.T) * (p.H / 8);
   moe_finalize_kernel<<<static_cast<unsigned>((nthreads + 255) / 256), 256, 0, s>>>(p);
   if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();

@@ -44,7 +44,7 @@ struct FwdBuffers {
   uint8_t* a2_scales;
   float* a2_g;
   _Float16* a2q16;
-  float* y;
+  uint16_t* y;  // bf16
   float* out_acc;
   // library copies of the per-expert global scales (own_gscales)
   float* w13g;

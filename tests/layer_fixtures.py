@@ -46,6 +46,8 @@ def check_layer_tolerance(got, ref):
     d = np.abs(got - ref)
     raw = d.max() / rms
     mx = (d - bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))).max() / rms
+    print(f"layer tolerance: rel {rel:.3e}, max/rms beyond rounding {mx:.3e} (raw {raw:.3e}), "
+          f"{got.size} outputs", file=sys.stderr, flush=True)
     assert rel <= TOL_REL and mx <= TOL_MAX_RMS, f"rel {rel:.3e}, max/rms beyond rounding {mx:.3e} (raw {raw:.3e})"
     return rel, mx
 
