@@ -547,6 +547,166 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
 }
 
 // ---------------------------------------------------------------------------
+// Prologue for large batches with E <= 256 and T <= 8192, two kernels.
+//  1. route64: blocks 0 .. nr-1 route 64 tokens each (16 lanes per token, the
+//     small-batch router, four tokens per wave in one pass) and rank every
+//     (t, j) among the block's equal experts (ballots over 64-entry chunks,
+//     then a scan of the chunk counts per expert), writing the block's
+//     per-expert counts; blocks nr.. quantize 16 token rows each, one per
+//     wave, at the same time.
+//  2. place64 (one block per routing block, one thread per (t, j)): every
+//     block sums the count matrix per expert, over all routing blocks (the
+//     totals, scanned over the experts for the row offsets) and over the
+//     blocks before its own (its base), then row = offset[e] + base[e] +
+//     rank; block 0 also publishes counts, offsets, the tile count and the
+//     M-tile list.  Same stable order as the other prologues.
+// ---------------------------------------------------------------------------
+constexpr int kRoute64Tokens = 64;
+constexpr int kRoute64MaxE = 256;
+constexpr int kRoute64MaxT = 8192;
+static_assert(kRoute64Tokens * kMaxTopK <= kSmallThreads, "one thread per (t, j) of a routing block");
+
+bool use_route64_prologue(const FwdParams& p) { return p.E <= kRoute64MaxE && p.T <= kRoute64MaxT; }
+
+template <int NB, int KPL>
+__global__ __launch_bounds__(kSmallThreads) void moe_route64_kernel(FwdParams p, int nr) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int H = p.H, k = p.k, E = p.E, T = p.T;
+  if (static_cast<int>(blockIdx.x) >= nr) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x - nr) * kSmallWaves + wave;
+    if (t < T) {
+      if (p.preq) {  // codes handed over: only the tiled GEMMs' fp16 copy is written
+        if (p.xq16)
+          dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H, lane,
+                          kWave);
+      } else if (!p.a16) {  // (W4A16 uses x as it is)
+        quantize_row_wave<NB>(p.x + t * H, H / 16, p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16),
+                              p.xq_g + t, lane, p.xq16 ? p.xq16 + t * H : nullptr, p.static_g);
+      }
+      if (!p.deterministic) {
+        float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+        for (int c = lane; c < H / 4; c += kWave) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
+  constexpr int kN = kRoute64Tokens * kMaxTopK;
+  __shared__ int32_t s_ids[kN];
+  __shared__ int32_t s_rank[kN];
+  __shared__ int32_t s_cnt[kN / 64][kRoute64MaxE];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x, t0 = b * kRoute64Tokens;
+  const int ntok = min(kRoute64Tokens, T - t0), n = ntok * k;
+  // 1. routing: wave w, group g routes token t0 + 4 w + g
+  const int grp = lane >> 4, gl = lane & 15;
+  {
+    const int lt = 4 * wave + grp;
+    const int tc = t0 + min(lt, ntok - 1);
+    int id;
+    float w;
+    route_token_group16<KPL>(p.logits + static_cast<int64_t>(tc) * E, E, k, gl, id, w);
+    if (lt < ntok && gl < k) {
+      const int64_t i = static_cast<int64_t>(t0 + lt) * k + gl;
+      p.topk_ids[i] = id;
+      p.topk_w[i] = w;
+      s_ids[lt * k + gl] = id;
+    }
+  }
+  for (int i = tid; i < (kN / 64) * kRoute64MaxE; i += kSmallThreads) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  // 2. ranks inside 64-entry chunks
+  const int nch = (n + 63) / 64;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  if (wave < nch) {
+    const int i = 64 * wave + lane;
+    const bool valid = i < n;
+    const int e = valid ? s_ids[i] : 0;
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bm = __ballot((e >> bit) & 1);
+      mask &= ((e >> bit) & 1) ? bm : ~bm;
+    }
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    if (valid) {
+      s_rank[i] = rank;
+      if (rank == 0) s_cnt[wave][e] = __popcll(mask);
+    }
+  }
+  __syncthreads();
+  // 3. per expert: exclusive scan down the chunks; the block's count
+  if (tid < E) {
+    int tot = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int v = s_cnt[c][tid];
+      s_cnt[c][tid] = tot;
+      tot += v;
+    }
+    p.blk_counts[static_cast<int64_t>(b) * E + tid] = tot;
+  }
+  __syncthreads();
+  // 4. rank among the block's equal experts, in (t, j) order
+  if (tid < n) p.loc_rank[static_cast<int64_t>(t0) * k + tid] = s_cnt[tid / 64][s_ids[tid]] + s_rank[tid];
+}
+
+__global__ __launch_bounds__(kSmallThreads) void moe_place64_kernel(FwdParams p, int nr) {
+  constexpr int kParts = kSmallThreads / kRoute64MaxE;  // threads per expert summing the counts
+  __shared__ int32_t s_pre[kParts][kRoute64MaxE];
+  __shared__ int32_t s_all[kParts][kRoute64MaxE];
+  __shared__ int32_t s_base[kRoute64MaxE];
+  __shared__ int s_tot[2][4];
+  const int tid = threadIdx.x, E = p.E, k = p.k, mt = p.mt;
+  const int b = blockIdx.x;
+  const int e = tid % kRoute64MaxE, q = tid / kRoute64MaxE;
+  int pre = 0, all = 0;
+  if (e < E) {
+    for (int r = q; r < nr; r += kParts) {
+      const int c = p.blk_counts[static_cast<int64_t>(r) * E + e];
+      all += c;
+      pre += r < b ? c : 0;
+    }
+  }
+  s_pre[q][e] = pre;
+  s_all[q][e] = all;
+  __syncthreads();
+  // threads 0..255: expert tid's total and base, then the scans over experts
+  int cnt = 0, base = 0;
+  if (tid < kRoute64MaxE && tid < E) {
+#pragma unroll
+    for (int i = 0; i < kParts; ++i) {
+      cnt += s_all[i][tid];
+      base += s_pre[i][tid];
+    }
+  }
+  const int ntile = (cnt + mt - 1) / mt;
+  int rb = cnt, tb = ntile;
+  const int2 total = scan256_pair(rb, tb, tid, s_tot);
+  if (tid < kRoute64MaxE && tid < E) {
+    const int off = rb - cnt;
+    s_base[tid] = off + base;
+    if (b == 0) {
+      p.counts[tid] = cnt;
+      p.offsets[tid] = off;
+      const int t0 = tb - ntile;
+      for (int i = 0; i < ntile; ++i) p.tiles[t0 + i] = make_int4(tid, off + i * mt, min(mt, cnt - i * mt), 0);
+    }
+  }
+  if (b == 0 && tid == kRoute64MaxE - 1) {
+    p.offsets[E] = total.x;
+    *p.n_tiles = append_shared_tiles(p, total.y);
+  }
+  __syncthreads();
+  const int t0 = b * kRoute64Tokens;
+  const int n = min(kRoute64Tokens, p.T - t0) * k;
+  if (tid < n) {
+    const int64_t i = static_cast<int64_t>(t0) * k + tid;
+    const int row = s_base[p.topk_ids[i]] + p.loc_rank[i];
+    p.perm[row] = static_cast<int32_t>(i);
+    p.inv[i] = row;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Prologue for decode-sized batches (T <= 64, E <= 256): block 0 routes every
 // token (a whole wave per token up to kTinyWaveRouteT tokens, else 16 lanes
 // per token, all tokens in one pass) and keeps, per expert,
@@ -878,6 +1038,18 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
   moe_place_kernel<<<(p.R + 255) / 256, 256, 0, s>>>(p, tpb);
 }
 
+template <int NB>
+static void launch_route64(const FwdParams& p, hipStream_t s) {
+  const int nr = (p.T + kRoute64Tokens - 1) / kRoute64Tokens;
+  const int nq = (p.T + kSmallWaves - 1) / kSmallWaves;
+  if (p.E <= 16) moe_route64_kernel<NB, 1><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 32) moe_route64_kernel<NB, 2><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 64) moe_route64_kernel<NB, 4><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 128) moe_route64_kernel<NB, 8><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else moe_route64_kernel<NB, 16><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  moe_place64_kernel<<<nr, kSmallThreads, 0, s>>>(p, nr);
+}
+
 hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
                               hipEvent_t const* ev) {
   if (ev) (void)hipEventRecord(ev[0], s);
@@ -894,6 +1066,14 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
       case 4: launch_prologue_small<4>(p, s); break;
       case 8: launch_prologue_small<8>(p, s); break;
       default: launch_prologue_small<0>(p, s); break;
+    }
+  } else if (use_route64_prologue(p)) {
+    switch (quant_nb_for_cols(p.H)) {
+      case 1: launch_route64<1>(p, s); break;
+      case 2: launch_route64<2>(p, s); break;
+      case 4: launch_route64<4>(p, s); break;
+      case 8: launch_route64<8>(p, s); break;
+      default: launch_route64<0>(p, s); break;
     }
   } else {
     const int tpb = route_tokens_per_block(p.T);
