@@ -546,14 +546,81 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_small_kernel(FwdPa
   }
 }
 
+// Per-token quantization of one row per 256 threads of a 1024-thread block
+// (row t; thread qt = tid % 256 owns 16-element blocks qt, qt + 256, ...; the
+// row amax is one LDS exchange between the quarter's four waves).  Every
+// thread of the block calls it (one barrier); a quarter with t >= T only
+// joins the barrier.  Also clears the row's atomic accumulator, or (codes
+// handed over) writes only the tiled GEMMs' fp16 copy.
+template <int NBL>
+__device__ __forceinline__ void prologue_quantize_quarter(const FwdParams& p, int64_t t, int tid) {
+  __shared__ float s_am[kSmallWaves];
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const int qt = tid & 255, q = tid >> 8;
+  const int H = p.H, T = p.T;
+  if (p.a16 || p.preq) {  // W4A16 uses x as it is; handed-over codes only need the fp16
+                          // copy of the tiled GEMMs (if any) and the atomic accumulator cleared
+    if (t < T && p.preq && p.xq16)
+      dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H, qt, 256);
+    if (t < T && !p.deterministic) {
+      float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+      for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const int nblk = H / 16;
+  const uint16_t* xrow = p.x + min(t, static_cast<int64_t>(T - 1)) * H;
+  uint4 v[NBL][2];
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const uint4* src = reinterpret_cast<const uint4*>(xrow + 16 * min(qt + 256 * i, nblk - 1));
+    v[i][0] = src[0];
+    v[i][1] = src[1];
+  }
+  float bam[NBL];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    bam[i] = amax16_bf16(v[i][0], v[i][1]);
+    if (qt + 256 * i < nblk) am = fmaxf(am, bam[i]);
+  }
+  am = wave_max(am);
+  if (lane == 0) s_am[wave] = am;
+  __syncthreads();
+  if (t >= T) return;
+  const float* sq = s_am + 4 * q;
+  const float g = p.static_g ? p.static_g[0] : global_scale(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3])));
+  uint8_t* crow = p.xq_codes + t * (H / 2);
+  uint8_t* srow = p.xq_scales + t * (H / 16);
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int b = qt + 256 * i;
+    if (b < nblk) {
+      float f[16];
+      unpack16(v[i][0], v[i][1], f);
+      uint32_t lo, hi;
+      const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
+      *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
+      srow[b] = static_cast<uint8_t>(sb);
+      if (p.xq16) store_block_f16(p.xq16 + t * H + 16 * b, lo, hi, sb);
+    }
+  }
+  if (qt == 0) p.xq_g[t] = g;
+  if (!p.deterministic) {
+    float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
+    for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prologue for large batches with E <= 256 and T <= 8192, two kernels.
 //  1. route64: blocks 0 .. nr-1 route 64 tokens each (16 lanes per token, the
 //     small-batch router, four tokens per wave in one pass) and rank every
 //     (t, j) among the block's equal experts (ballots over 64-entry chunks,
 //     then a scan of the chunk counts per expert), writing the block's
-//     per-expert counts; blocks nr.. quantize 16 token rows each, one per
-//     wave, at the same time.
+//     per-expert counts; blocks nr.. quantize token rows at the same time:
+//     16 per block, one per wave, or (rows of more than 4096 elements, QB >
+//     0) 4 per block, one per 256 threads.
 //  2. place64 (one block per routing block, one thread per (t, j)): every
 //     block sums the count matrix per expert, over all routing blocks (the
 //     totals, scanned over the experts for the row offsets) and over the
@@ -568,10 +635,15 @@ static_assert(kRoute64Tokens * kMaxTopK <= kSmallThreads, "one thread per (t, j)
 
 bool use_route64_prologue(const FwdParams& p) { return p.E <= kRoute64MaxE && p.T <= kRoute64MaxT; }
 
-template <int NB, int KPL>
+template <int NB, int KPL, int QB>
 __global__ __launch_bounds__(kSmallThreads) void moe_route64_kernel(FwdParams p, int nr) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int H = p.H, k = p.k, E = p.E, T = p.T;
+  if (QB > 0 && static_cast<int>(blockIdx.x) >= nr) {
+    prologue_quantize_quarter<(QB > 0 ? QB : 1)>(p, static_cast<int64_t>(blockIdx.x - nr) * 4 + (threadIdx.x >> 8),
+                                                  threadIdx.x);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) >= nr) {
     const int64_t t = static_cast<int64_t>(blockIdx.x - nr) * kSmallWaves + wave;
     if (t < T) {
@@ -660,10 +732,18 @@ __global__ __launch_bounds__(kSmallThreads) void moe_place64_kernel(FwdParams p,
   const int e = tid % kRoute64MaxE, q = tid / kRoute64MaxE;
   int pre = 0, all = 0;
   if (e < E) {
-    for (int r = q; r < nr; r += kParts) {
-      const int c = p.blk_counts[static_cast<int64_t>(r) * E + e];
-      all += c;
-      pre += r < b ? c : 0;
+    // rows q, q + kParts, ... in batches of kU loads issued together
+    constexpr int kU = 16;
+    for (int r0 = q; r0 < nr; r0 += kParts * kU) {
+      int c[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c[u] = p.blk_counts[static_cast<int64_t>(min(r0 + kParts * u, nr - 1)) * E + e];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int r = r0 + kParts * u;
+        all += r < nr ? c[u] : 0;
+        pre += r < b ? c[u] : 0;
+      }
     }
   }
   s_pre[q][e] = pre;
@@ -725,61 +805,7 @@ __global__ __launch_bounds__(kSmallThreads) void moe_prologue_tiny_kernel(FwdPar
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int H = p.H, k = p.k, E = p.E, T = p.T;
   if (blockIdx.x > 0) {
-    __shared__ float s_am[kSmallWaves];
-    const int q = tid >> 8, qt = tid & 255;  // quarter of the block and thread within it
-    const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * 4 + q;
-    if (p.a16 || p.preq) {  // W4A16 uses x as it is; handed-over codes only need the fp16
-                            // copy of the tiled GEMMs (if any) and the atomic accumulator cleared
-      if (t < T && p.preq && p.xq16)
-        dequant_row_f16(p.xq_codes + t * (H / 2), p.xq_scales + t * (H / 16), H / 16, p.xq16 + t * H, qt, 256);
-      if (t < T && !p.deterministic) {
-        float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
-        for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      return;
-    }
-    const int nblk = H / 16;
-    const uint16_t* xrow = p.x + min(t, static_cast<int64_t>(T - 1)) * H;
-    uint4 v[NBL][2];
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) {
-      const uint4* src = reinterpret_cast<const uint4*>(xrow + 16 * min(qt + 256 * i, nblk - 1));
-      v[i][0] = src[0];
-      v[i][1] = src[1];
-    }
-    float bam[NBL];
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) {
-      bam[i] = amax16_bf16(v[i][0], v[i][1]);
-      if (qt + 256 * i < nblk) am = fmaxf(am, bam[i]);
-    }
-    am = wave_max(am);
-    if (lane == 0) s_am[wave] = am;
-    __syncthreads();
-    if (t >= T) return;
-    const float* sq = s_am + 4 * q;
-    const float g = p.static_g ? p.static_g[0] : global_scale(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3])));
-    uint8_t* crow = p.xq_codes + t * (H / 2);
-    uint8_t* srow = p.xq_scales + t * (H / 16);
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) {
-      const int b = qt + 256 * i;
-      if (b < nblk) {
-        float f[16];
-        unpack16(v[i][0], v[i][1], f);
-        uint32_t lo, hi;
-        const uint32_t sb = quantize_block16_amax(f, bam[i], g, lo, hi);
-        *reinterpret_cast<uint2*>(crow + 8 * b) = make_uint2(lo, hi);
-        srow[b] = static_cast<uint8_t>(sb);
-        if (p.xq16) store_block_f16(p.xq16 + t * H + 16 * b, lo, hi, sb);
-      }
-    }
-    if (qt == 0) p.xq_g[t] = g;
-    if (!p.deterministic) {
-      float4* row = reinterpret_cast<float4*>(p.out_acc + t * H);
-      for (int c = qt; c < H / 4; c += 256) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    prologue_quantize_quarter<NBL>(p, static_cast<int64_t>(blockIdx.x - 1) * 4 + (tid >> 8), tid);
     return;
   }
   __shared__ uint64_t s_mask[kTinyMaxE];
@@ -1038,15 +1064,18 @@ static void launch_route(const FwdParams& p, int nblocks, int tpb, hipStream_t s
   moe_place_kernel<<<(p.R + 255) / 256, 256, 0, s>>>(p, tpb);
 }
 
-template <int NB>
+// NB: row registers of the one-row-per-wave quantizer; QB > 0: rows of more
+// than 256 blocks of 16 use the one-row-per-256-threads quantizer with QB
+// blocks per thread (more rows in flight per CU).
+template <int NB, int QB>
 static void launch_route64(const FwdParams& p, hipStream_t s) {
   const int nr = (p.T + kRoute64Tokens - 1) / kRoute64Tokens;
-  const int nq = (p.T + kSmallWaves - 1) / kSmallWaves;
-  if (p.E <= 16) moe_route64_kernel<NB, 1><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
-  else if (p.E <= 32) moe_route64_kernel<NB, 2><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
-  else if (p.E <= 64) moe_route64_kernel<NB, 4><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
-  else if (p.E <= 128) moe_route64_kernel<NB, 8><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
-  else moe_route64_kernel<NB, 16><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  const int nq = QB > 0 ? (p.T + 3) / 4 : (p.T + kSmallWaves - 1) / kSmallWaves;
+  if (p.E <= 16) moe_route64_kernel<NB, 1, QB><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 32) moe_route64_kernel<NB, 2, QB><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 64) moe_route64_kernel<NB, 4, QB><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else if (p.E <= 128) moe_route64_kernel<NB, 8, QB><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
+  else moe_route64_kernel<NB, 16, QB><<<nr + nq, kSmallThreads, 0, s>>>(p, nr);
   moe_place64_kernel<<<nr, kSmallThreads, 0, s>>>(p, nr);
 }
 
@@ -1068,13 +1097,14 @@ hipError_t launch_moe_forward(const FwdParams& p, int max_tiles, hipStream_t s,
       default: launch_prologue_small<0>(p, s); break;
     }
   } else if (use_route64_prologue(p)) {
-    switch (quant_nb_for_cols(p.H)) {
-      case 1: launch_route64<1>(p, s); break;
-      case 2: launch_route64<2>(p, s); break;
-      case 4: launch_route64<4>(p, s); break;
-      case 8: launch_route64<8>(p, s); break;
-      default: launch_route64<0>(p, s); break;
-    }
+    const int nblk = p.H / 16;
+    if (nblk <= 64) launch_route64<1, 0>(p, s);
+    else if (nblk <= 128) launch_route64<2, 0>(p, s);
+    else if (nblk <= 256) launch_route64<4, 0>(p, s);
+    else if (nblk <= 512) launch_route64<1, 2>(p, s);
+    else if (nblk <= 1024) launch_route64<1, 4>(p, s);
+    else if (nblk <= 2048) launch_route64<1, 8>(p, s);
+    else launch_route64<0, 0>(p, s);
   } else {
     const int tpb = route_tokens_per_block(p.T);
     const int nblocks = (p.T + tpb - 1) / tpb;
