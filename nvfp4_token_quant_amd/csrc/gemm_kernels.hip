@@ -70,8 +70,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // for row m = 16 fm + r16; ginv[fm] = 1 / (that row's token global scale),
 // wginv = 1 / (the expert's W13 global scale).
 // act = silu(h_gate) * h_up in fp32, stored with the row's amax over these
-// columns in s_amax[wave][m].
-template <int FM, int FNH, int SM = 16 * FM>
+// columns in s_amax[wave][m].  BF16: W4A16's GEMM2 input, act rounded to
+// bf16 (nearest even), is stored as well (a2q16, the same index).
+template <int FM, int FNH, int SM = 16 * FM, bool BF16 = false>
 __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&acc)[2 * FNH][FM],
                                             int e, int row0, int nrows, int c0, const float (&ginv)[FM],
                                             float (*s_amax)[SM], int wave, int g, int r16, float wginv) {
@@ -94,8 +95,17 @@ __device__ __forceinline__ void g1_epilogue(const FwdParams& p, const f32x4 (&ac
       }
       if (m < nrows) {
         const int n = c0 + fh * 16 + 4 * g;
-        *reinterpret_cast<float4*>(p.act + static_cast<int64_t>(row0 + m) * p.I + n) =
-            make_float4(a[0], a[1], a[2], a[3]);
+        const int64_t idx = static_cast<int64_t>(row0 + m) * p.I + n;
+        *reinterpret_cast<float4*>(p.act + idx) = make_float4(a[0], a[1], a[2], a[3]);
+        if constexpr (BF16) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 r;
+          r[0] = static_cast<__bf16>(a[0]);
+          r[1] = static_cast<__bf16>(a[1]);
+          r[2] = static_cast<__bf16>(a[2]);
+          r[3] = static_cast<__bf16>(a[3]);
+          *reinterpret_cast<bf16x4*>(p.a2q16 + idx) = r;
+        }
       }
     }
     am = fmaxf(am, __shfl_xor(am, 16, kWave));
@@ -952,7 +962,9 @@ __device__ __forceinline__ void tiled_tile(const FwdParams& p, TiledShared<TR>& 
   }
   if constexpr (MODE == 0) {
     if (has_unit) {
-      g1_epilogue<FMV, 2, TR>(p, acc, b.e, row0, nrows, 32 * j, ginv, sh.amax, wave, g, r16, wginv);
+      // (W4A16 with 128-row tiles: the tiled GEMM2 reads the bf16 copy)
+      g1_epilogue<FMV, 2, TR, A16 && TR == kTiledRows>(p, acc, b.e, row0, nrows, 32 * j, ginv, sh.amax, wave, g,
+                                                      r16, wginv);
     } else if (g == 0) {
 #pragma unroll
       for (int fm = 0; fm < FMV; ++fm) sh.amax[wave][fm * 16 + r16] = 0.0f;
@@ -1042,23 +1054,6 @@ void moe_tiled_kernel(FwdParams p) {
     else
       tiled_tile<1, MODE, A16, TR>(p, sh, b, wb, my_g, my_slot, wg);
   }
-}
-
-// ---------------------------------------------------------------------------
-// W4A16: GEMM2's input is act rounded to bf16 (nearest even), 8 values per
-// thread into the 16-bit operand buffer the tiled GEMM2 reads.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void moe_act_bf16_kernel(FwdParams p) {
-  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
-  if (i >= static_cast<int64_t>(p.Rt) * p.I) return;
-  const float4* src = reinterpret_cast<const float4*>(p.act + i);
-  const float4 a = src[0], b = src[1];
-  bf16x8 r;
-  r[0] = static_cast<__bf16>(a.x); r[1] = static_cast<__bf16>(a.y);
-  r[2] = static_cast<__bf16>(a.z); r[3] = static_cast<__bf16>(a.w);
-  r[4] = static_cast<__bf16>(b.x); r[5] = static_cast<__bf16>(b.y);
-  r[6] = static_cast<__bf16>(b.z); r[7] = static_cast<__bf16>(b.w);
-  *reinterpret_cast<bf16x8*>(p.a2q16 + i) = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -1246,10 +1241,9 @@ hipError_t launch_grouped_gemms(const FwdParams& p, int max_tiles, hipStream_t s
     // token rows are then fetched into one L2)
     const int gx = (max_tiles + 7) / 8 * 8;  // == p.tiled_gx
     if (p.a16) {
+      // (GEMM1's epilogue also writes GEMM2's bf16 input)
       moe_tiled_kernel<0, true><<<gx * nb1, kTiledThreads, 0, s>>>(p);
       if (ev) (void)hipEventRecord(ev[2], s);
-      const int64_t n8 = static_cast<int64_t>(p.Rt) * p.I / 8;
-      moe_act_bf16_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, s>>>(p);
       moe_tiled_kernel<1, true><<<gx * nb2, kTiledThreads, 0, s>>>(p);
     } else {
       moe_tiled_kernel<0, false><<<gx * nb1, kTiledThreads, 0, s>>>(p);
