@@ -306,7 +306,7 @@ int moe_nvfp4_forward_quantized(moe_workspace* ws, const void* x_codes_dev, cons
  *                with its global-scale arrays for the call's duration
  *   x_dev, logits_dev, T, out_dev, stream   as for moe_nvfp4_forward
  * A forward whose intermediates exceed the array (for example more than
- * about 590 tokens of a 2048 x 768 x 128-expert top-8 layer, about 180 of a
+ * about 840 tokens of a 2048 x 768 x 128-expert top-8 layer, about 270 of a
  * 7168 x 2048 x 256-expert one) returns NVFP4_ERR_INVALID_ARG, naming the
  * largest token count that fits, and launches nothing.  All calls on one GPU
  * share that GPU's array, and it keeps the last call's contents: calls that
