@@ -67,12 +67,15 @@ LAYERS = {
     # prologues take, the largest top-k, an odd number of K steps and a
     # GEMM2 unit count not divisible by four; the tiled GEMMs with partial
     # column bands; the largest expert count; 256 experts on small shapes
-    # (both routers of the one-block prologue on the most keys per lane).
+    # (both routers of the one-block prologue on the most keys per lane);
+    # the largest top-k on the 64-token routing blocks (1024 (t, j) entries
+    # per block) with the tiled GEMMs.
     6: Layer(6, "edge-single", 9, 128, 1, 1, 128, 0.02, 16),
     7: Layer(7, "edge-wide", 33, 384, 300, 16, 384, 0.02, 64),
     8: Layer(8, "edge-tiled", 700, 640, 6, 3, 256, 0.02, 1024),
     9: Layer(9, "edge-experts", 3, 256, 1024, 16, 128, 0.02, 8),
     10: Layer(10, "edge-router", 8, 128, 256, 8, 128, 0.02, 64),
+    11: Layer(11, "edge-topk16", 300, 256, 64, 16, 128, 0.02, 512),
 }
 
 

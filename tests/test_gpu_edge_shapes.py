@@ -2,7 +2,8 @@
 oracle on every token: one expert with one K step in both GEMMs (and K ranges
 split over waves that get no step); 300 experts (past the one-launch
 prologues), top-16, three K steps, six GEMM2 units (not a multiple of four);
-the tiled GEMMs with partial column bands and odd K steps; 1024 experts.
+the tiled GEMMs with partial column bands and odd K steps; 1024 experts;
+top-16 on the 64-token routing blocks with the tiled GEMMs.
 
 Bit-exact: the per-token quantization, router ids, the permutation, the
 re-quantization of every expanded row (NVFP4) or GEMM2's bf16 input
@@ -19,7 +20,7 @@ from tests.layer_fixtures import (bf16_tensor_to_f64, check_layer_tolerance, gpu
 pytestmark = pytest.mark.gpu
 
 CASES = [(6, "nvfp4"), (6, "w4a16"), (7, "nvfp4"), (7, "atomic"), (7, "shared"), (8, "nvfp4"),
-         (8, "w4a16"), (8, "shared"), (9, "nvfp4")]
+         (8, "w4a16"), (8, "shared"), (9, "nvfp4"), (11, "nvfp4"), (11, "atomic"), (11, "shared")]
 
 
 @pytest.mark.parametrize("layer_id,mode", CASES)

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 100), (1, 300), (1, 5), (2, 8), (2, 64), (10, 8),
-                                        (10, 40), (9, 3), (2, 300), (10, 520), (7, 300)])
+                                        (10, 40), (9, 3), (2, 300), (10, 520), (7, 300), (11, 300)])
 def test_router_ties_and_signed_zeros(layer_id, T):
     L = synth.LAYERS[layer_id]
     print(f"layer {layer_id} tied logits T={T}", flush=True)
