@@ -6,11 +6,10 @@ index with the slots in that order, exactly as the oracle's router decides.
 Covered on the four prologue paths (one block routing every token for
 T <= 64, with a whole wave per token up to 8 tokens and 16 lanes per token
 above; the small-batch block for T <= 256; routing blocks of 64 tokens for
-up to 256 experts and 8192 tokens, a last block of fewer tokens included;
-the three-kernel schedule past those) and with 1 to 16 keys per lane (8 to
-1024 experts): router ids and weights,
-the stable expandInputRows permutation, and the layer output against the
-oracle.
+up to 256 experts and 8192 tokens, a last block of fewer tokens, down to
+one, included; the three-kernel schedule past those) and with 1 to 16 keys
+per lane (8 to 1024 experts): router ids and weights, the stable
+expandInputRows permutation, and the layer output against the oracle.
 """
 import numpy as np
 import pytest
@@ -25,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("layer_id,T", [(1, 16), (1, 100), (1, 300), (1, 5), (2, 8), (2, 64), (10, 8),
-                                        (10, 40), (9, 3), (2, 300), (10, 520), (7, 300), (11, 300)])
+                                        (10, 40), (9, 3), (2, 300), (10, 520), (7, 300), (11, 300), (11, 129)])
 def test_router_ties_and_signed_zeros(layer_id, T):
     L = synth.LAYERS[layer_id]
     print(f"layer {layer_id} tied logits T={T}", flush=True)
