@@ -17,14 +17,15 @@ Timing: `steps` forwards after `warmup` untimed ones, bracketed by
 synchronizations; wall time gives `value` (tokens/s).  By default the timed
 forwards are captured into one HIP graph and replayed once (a decode
 deployment replays one graph per model step holding every layer; `--eager`
-launches the kernels directly); after the graph replay the same forwards are
-also timed launched directly, without stage events (`eager_ms_per_step`,
-reported beside `ms_per_step`).  Every timed forward
-records HIP events around its four kernels on its own stream, which give
-each kernel's mean duration; the dominant kernel's algorithmic bytes (or
-FLOPs) over that duration is `roofline.achieved`.  Expert weights rotate over
-`--rotate` copies so consecutive steps do not find them in the 256 MB
-Infinity Cache.
+launches the kernels directly).  After the graph replay the same forwards
+are timed a second time, launched directly, each recording HIP events
+around its four kernels on its own stream (`eager_ms_per_step`, reported
+beside `ms_per_step`): those intervals give each kernel's mean duration, and
+the dominant kernel's algorithmic bytes (or FLOPs) over that duration is
+`roofline.achieved`.  (A HIP graph's event-record nodes leave the events'
+timestamps as their last eager record had them, so the graph replay itself
+cannot time its kernels.)  Expert weights rotate over `--rotate` copies so
+consecutive steps do not find them in the 256 MB Infinity Cache.
 """
 import argparse
 import ctypes
@@ -252,45 +253,10 @@ def bench_layer(args, layer_id, T, cpu_budget_s):
     torch.cuda.synchronize()
     lib = binding.lib()
     lib.moe_workspace_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
-    if not args.eager:
-        # The timed forwards are captured into one HIP graph (each forward with
-        # its own stage events, recorded by the graph on every replay), the
-        # warm-up forwards into another; a decode deployment likewise replays
-        # one graph per model step holding every layer.
-        evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
-        warm_evs = [[hip.event() for _ in range(5)] for _ in range(max(args.warmup, 1))]
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-
-        def capture(ev_sets, first):
-            with torch.cuda.stream(cap):
-                for i, ev in enumerate(ev_sets):
-                    ly = layers[(first + i) % len(layers)]
-                    lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
-                    # record the events once outside the graph (HIP reports no
-                    # elapsed time for events only ever recorded by graph nodes)
-                    fwd(ly)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    for i, ev in enumerate(ev_sets):
-                        ly = layers[(first + i) % len(layers)]
-                        lib.moe_workspace_set_stage_events(ly.handle, (ctypes.c_void_p * 5)(*[e.value for e in ev]))
-                        fwd(ly)
-            return g
-
-        warm_graph = capture(warm_evs, 0)
-        graph = capture(evs, 0)
-        torch.cuda.synchronize()
-        warm_graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for ev in warm_evs:
-            for e in ev:
-                hip.destroy(e)
-    else:
+    def timed_eager():
+        """The K forwards launched directly, each recording its five stage
+        events on the forward's stream; returns the wall time and the mean
+        interval of each stage."""
         evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
         arrs = [(ctypes.c_void_p * 5)(*[e.value for e in step]) for step in evs]
         torch.cuda.synchronize()
@@ -301,30 +267,54 @@ def bench_layer(args, layer_id, T, cpu_budget_s):
             fwd(ly)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-    per_stage = {s: [] for s in stages}
-    for step in evs:
-        for j, s in enumerate(stages):
-            per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
-    for ly in layers:
-        lib.moe_workspace_set_stage_events(ly.handle, None)
-    mean_ms = {s: float(np.mean(v)) for s, v in per_stage.items()}
-    for step in evs:
-        for e in step:
-            hip.destroy(e)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = T * args.steps / (t1 - t0)
-    eager_ms = None
-    if not args.eager:
-        # the same forwards launched directly (no graph, no stage events), for
-        # reference next to the graph replay above
         for ly in layers:
             lib.moe_workspace_set_stage_events(ly.handle, None)
+        per_stage = {s: [] for s in stages}
+        for step in evs:
+            for j, s in enumerate(stages):
+                per_stage[s].append(hip.elapsed_ms(step[j], step[j + 1]))
+        for step in evs:
+            for e in step:
+                hip.destroy(e)
+        return t1 - t0, {s: float(np.mean(v)) for s, v in per_stage.items()}
+
+    eager_ms = None
+    if not args.eager:
+        # The timed forwards are captured into one HIP graph, the warm-up
+        # forwards into another; a decode deployment likewise replays one
+        # graph per model step holding every layer.  The graphs hold the
+        # kernels only: an event recorded by a HIP graph node keeps the
+        # timestamp of its last eager record on every replay (measured), so
+        # the stage durations come from the eager timed pass below.
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+
+        def capture(n, first):
+            with torch.cuda.stream(cap):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for i in range(n):
+                        fwd(layers[(first + i) % len(layers)])
+            return g
+
+        warm_graph = capture(max(args.warmup, 1), 0)
+        graph = capture(args.steps, 0)
         torch.cuda.synchronize()
-        e0 = time.perf_counter()
-        for i in range(args.steps):
-            fwd(layers[i % len(layers)])
+        warm_graph.replay()
         torch.cuda.synchronize()
-        eager_ms = (time.perf_counter() - e0) * 1e3 / args.steps
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall = t1 - t0
+        # the same forwards launched directly with their stage events: the
+        # second timed region, which gives each kernel's mean duration
+        eager_wall, mean_ms = timed_eager()
+        eager_ms = eager_wall * 1e3 / args.steps
+    else:
+        wall, mean_ms = timed_eager()
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T * args.steps / wall
 
     dominant = max(["gemm1", "gemm2"], key=lambda s: mean_ms[s])
     workload = f"nvfp4_moe_layer_{L.name}" + (f"_shared_{args.shared}" if args.shared else "") + \
