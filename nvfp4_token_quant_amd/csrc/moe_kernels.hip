@@ -221,7 +221,8 @@ __device__ void route_token_wave(const float* __restrict__ lrow, int E, int k, i
 }
 
 // ---------------------------------------------------------------------------
-// Prologue for large batches, three kernels.
+// Prologue for large batches past the two-kernel one below (more than 256
+// experts or 8192 tokens), three kernels.
 //  1. route: each block takes `tpb` consecutive tokens; each wave quantizes
 //     and routes tokens of the block, then the block computes, for every
 //     (t, j), its rank among equal experts inside the block and the block's
