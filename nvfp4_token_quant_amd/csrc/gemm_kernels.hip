@@ -816,8 +816,9 @@ struct TiledBlock {
 // columns of 16 rows, so a direct store or atomic would touch 16 rows x 4
 // column groups per instruction.  Instead each wave stages 32 rows of its 64
 // columns in LDS (the token buffers, free after the K loop) and reads them
-// back row-major: a y store then writes 4 whole 256-byte row segments per
-// instruction, an atomic (w * y into out_acc) one whole row segment.
+// back row-major: a (bf16) y store then writes 8 whole 128-byte row
+// segments per instruction, an atomic (w * y into out_acc) one whole 256-byte
+// row segment.
 // Called by every wave of the block (barriers).
 template <int FMV>
 __device__ __forceinline__ void tiled_g2_staged(const FwdParams& p, TiledShared<kTiledRows>& sh,
